@@ -1,0 +1,240 @@
+"""Benchmark of the fused layer-half launch (mono_ffn_layer) on one MI355X.
+
+A step is one pass of the whole hot path over one batch: mHC mix -> split/Sinkhorn ->
+collapse + RMSNorm -> router + top-k -> shared and routed SwiGLU experts -> block -> expand ->
+carry of the next layer half's mix sums, as ONE persistent launch, with inputs resident in HBM.
+
+Headline workload: the V4.1-like layer half at 1 row with bf16 experts (hidden 5120, 256
+experts top-8, inter 2048, shared inter 2048). The 6-row Q8_0 workload is measured in the same
+run and reported under "rows6". Steps rotate over `--copies` independent weight copies and 64
+seeded input states, so routing changes every step and no weight is re-read from the 256 MB
+last-level cache; each step's algorithmic bytes count every distinct selected expert once.
+
+Prints ONE JSON line (rank 0, N = 1 only).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "MoE decode layer steps/s and achieved HBM GB/s (% peak) at 1 and 6 rows"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dense_bytes(cfg, carry: bool) -> int:
+    H, E = cfg.hidden, cfg.n_experts
+    ab = 4 if cfg.act == "f32" else 2
+    b = 24 * 4 * H * 4 * (2 if carry else 1)       # w_mix (+ the next layer's, for the carry)
+    b += E * H * 4 + E * 4 + H * ab + 3 * 4 + 24 * 4  # router, bias, norm weight, hc params
+    return b
+
+
+def step_bytes(cfg, idx_rows: np.ndarray, carry: bool) -> int:
+    import synth
+    per_routed = synth.expert_bytes(cfg.routed_fmt, cfg.inter, cfg.hidden)
+    per_shared = synth.expert_bytes(cfg.shared_fmt, cfg.shared_inter, cfg.hidden)
+    n_distinct = len(np.unique(idx_rows))
+    return n_distinct * per_routed + (per_shared if cfg.shared_inter else 0) + dense_bytes(cfg, carry)
+
+
+class Workload:
+    def __init__(self, cfg, copies: int):
+        import torch
+        import support
+        import moe_decode_layer_amd as mono
+        import synth.device as sdev
+        self.cfg, self.copies = cfg, copies
+        t0 = time.time()
+        self.layers = [sdev.layer(cfg, l) for l in range(copies)]
+        self.structs = [support.layer_struct(cfg, d) for d in self.layers]
+        self.states = [sdev.state(cfg, s) for s in range(64)]
+        self.shape = support.shape_of(cfg)
+        self.ws = torch.zeros(mono.mono_workspace_bytes(self.shape), dtype=torch.uint8,
+                              device="cuda")
+        mono.mono_workspace_init(self.ws, self.shape, support.stream())
+        ab = 4 if cfg.act == "f32" else 2
+        self.out = torch.zeros(cfg.rows * 4 * cfg.hidden * ab, dtype=torch.uint8, device="cuda")
+        self.carry = torch.zeros(cfg.rows * 25 * 4, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        log("  %s: %d weight copies resident (%.1f GB) in %.1f s" % (
+            cfg.name, copies, copies * self.weight_gb(), time.time() - t0))
+
+    def weight_gb(self) -> float:
+        import synth
+        c = self.cfg
+        b = c.n_experts * synth.expert_bytes(c.routed_fmt, c.inter, c.hidden)
+        if c.shared_inter:
+            b += synth.expert_bytes(c.shared_fmt, c.shared_inter, c.hidden)
+        return (b + dense_bytes(c, False)) / 1e9
+
+    def launch(self, i: int):
+        import moe_decode_layer_amd as mono
+        import support
+        l = i % self.copies
+        nxt = self.layers[(l + 1) % self.copies]["w_mix"]
+        mono.mono_ffn_layer(self.shape, self.structs[l], nxt, self.states[i % 64], None, self.out,
+                            self.carry, self.ws, support.stream())
+
+    def selection(self, i: int) -> np.ndarray:
+        import moe_decode_layer_amd as mono
+        import support
+        self.launch(i)
+        import torch
+        torch.cuda.synchronize()
+        return support.ws_tensor(self.shape, self.ws, mono.MONO_T_IDX, np.int32,
+                                 (self.cfg.rows, self.cfg.top_k))
+
+    def run(self, steps: int, warmup: int):
+        import torch
+        # algorithmic bytes of every step (selection depends on layer copy and input)
+        nbytes = [step_bytes(self.cfg, self.selection(i), True) for i in range(steps)]
+        for i in range(warmup):
+            self.launch(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record()
+            self.launch(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        dur_ms = np.array([a.elapsed_time(b) for a, b in ev])
+        span_ms = ev[0][0].elapsed_time(ev[-1][1])
+        return dict(wall_s=wall, span_ms=span_ms, dur_ms=dur_ms, bytes=np.array(nbytes))
+
+
+def summarize(res, cfg):
+    dur = res["dur_ms"]
+    gbs = res["bytes"] / (dur * 1e-3) / 1e9
+    avg_ms = float(dur.mean())
+    return dict(
+        steps_per_s=len(dur) / (res["span_ms"] * 1e-3),
+        ms_per_step=res["span_ms"] / len(dur),
+        launch_us_median=float(np.median(dur) * 1e3), launch_us_p10=float(np.percentile(dur, 10) * 1e3),
+        launch_us_p90=float(np.percentile(dur, 90) * 1e3), launch_us_mean=avg_ms * 1e3,
+        bytes_per_step_mean=float(res["bytes"].mean()),
+        achieved_gbs=float(res["bytes"].mean() / (avg_ms * 1e-3) / 1e9),
+        achieved_gbs_median=float(np.median(gbs)))
+
+
+def cpu_baseline(cfg, budget_s: float):
+    """The oracle, timed on the host cores over whole layer-half steps of the same workload
+    (selected experts generated on the host outside the timed region)."""
+    import oracle
+    import synth
+    s = oracle.shape_of(cfg)
+    d0, d1 = synth.dense_host(cfg, 0), synth.dense_host(cfg, 1)
+    shared = synth.expert_host(cfg, 0, None)
+    done, spent = 0, 0.0
+    while spent < budget_s and done < 64:
+        st = synth.state_host(cfg, done)
+        # routing first (timed), then experts generated (untimed), then the rest (timed)
+        t0 = time.perf_counter()
+        mixes = oracle.mix(s, st, d0["w_mix"])
+        pre, post, comb = oracle.split(s, mixes, d0["hc_scale"], d0["hc_base"])
+        x, norm = oracle.collapse_norm(s, st, pre, d0["w_norm"])
+        lg = oracle.router_logits(s, norm, d0["w_router"])
+        idx, w, _ = oracle.select(s, lg, d0["bias"])
+        spent += time.perf_counter() - t0
+        ex = {int(e): synth.expert_host(cfg, 0, int(e)) for e in np.unique(idx)}
+        t0 = time.perf_counter()
+        m = oracle.moe(s, norm, idx, w, cfg.routed_fmt, ex, cfg.shared_fmt, shared)
+        oracle.expand(s, st, m["block"], post, comb, d1["w_mix"])
+        spent += time.perf_counter() - t0
+        done += 1
+    return dict(value=done / spent, unit="steps/s", cores=oracle.threads(), kind="oracle",
+                sample="%d full layer-half steps of the same workload (%s), %.1f s of oracle "
+                       "compute; expert weights generated outside the timed region"
+                       % (done, cfg.name, spent))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=4, help="independent weight copies rotated")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-rows6", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d "
+              "refused)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_decode_layer_amd as mono
+    import synth
+    mono.lib()  # fails loudly when the HIP library is not built
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    cfg1 = synth.CONFIGS[2]
+    log("building workloads")
+    w1 = Workload(cfg1, args.copies)
+    r1 = summarize(w1.run(args.steps, args.warmup), cfg1)
+    log("  1 row:", json.dumps(r1))
+    del w1
+    torch.cuda.empty_cache()
+    rows6 = None
+    if not args.no_rows6:
+        cfg6 = synth.CONFIGS[3]
+        w6 = Workload(cfg6, args.copies)
+        r6 = summarize(w6.run(args.steps, args.warmup), cfg6)
+        log("  6 rows:", json.dumps(r6))
+        rows6 = dict(workload=cfg6.name, rows=6, steps_per_s=r6["steps_per_s"],
+                     launch_us_median=r6["launch_us_median"], achieved_gbs=r6["achieved_gbs"],
+                     frac=r6["achieved_gbs"] / PEAK_HBM_GBS,
+                     bytes_per_step=r6["bytes_per_step_mean"])
+        del w6
+        torch.cuda.empty_cache()
+    cpu = None if args.no_cpu else cpu_baseline(cfg1, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": r1["steps_per_s"],
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r1["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg1.name, "rows": 1, "hidden": cfg1.hidden,
+                   "n_experts": cfg1.n_experts, "top_k": cfg1.top_k, "inter": cfg1.inter,
+                   "shared_inter": cfg1.shared_inter, "weights": "bf16",
+                   "weight_copies_rotated": args.copies, "inputs_rotated": 64,
+                   "launch": "mono_ffn_layer, one persistent launch per step"},
+        "roofline": {"bound": "hbm", "achieved": r1["achieved_gbs"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": r1["achieved_gbs"] / PEAK_HBM_GBS,
+                     "traffic": None},
+        "launch_us": {"median": r1["launch_us_median"], "p10": r1["launch_us_p10"],
+                      "p90": r1["launch_us_p90"], "mean": r1["launch_us_mean"]},
+        "bytes_per_step": r1["bytes_per_step_mean"],
+        "rows6": rows6,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -67,7 +67,7 @@ typedef enum {
 
 /* Shape of one layer-half step. Limits: 0 <= rows <= 8; n_streams == 4; hidden, inter and
  * shared_inter multiples of 256 (128 is accepted for inter and shared_inter when the expert
- * format is f32 or bf16); 1 <= top_k <= 16, top_k <= n_experts <= 1024; act f32 or bf16. */
+ * format is f32 or bf16); 1 <= top_k <= 16, top_k <= n_experts <= 512; act f32 or bf16. */
 typedef struct {
   int rows;         /* R: decode rows (tokens) in the step */
   int hidden;       /* H */
@@ -130,6 +130,14 @@ mono_status mono_workspace_poll(const void* ws, uint32_t err[4], void* stream);
 mono_status mono_workspace_set_debug(void* ws, uint32_t spin_limit_ticks, int32_t fault_wg,
                                      int32_t fault_phase, void* stream);
 
+/* Test hook: when enable != 0, later mono_ffn_layer launches on this workspace record, per
+ * workgroup, the 100 MHz real-time counter at phase boundaries (MONO_T_TRACE): 0 start,
+ * 1 mix partials, 2 pre-side inputs ready, 3 pre side, 4 router, 5 shared gate/up, 6 router
+ * barrier passed, 7 select, 8 plan, 9 routed gate/up, 10 gate/up barrier passed, 11 down +
+ * block, 12 expand, 13 carry; 14-18 inside the pre side (raw sums, mixes, gates, collapse,
+ * sum of squares), 19 select scores, 21 hidden rows staged. Enqueued on `stream`. */
+mono_status mono_workspace_set_trace(void* ws, int enable, void* stream);
+
 /* Intermediate tensors kept in the workspace by mono_ffn_layer (and by the unfused calls, for
  * the tensors they produce internally), for inspection after the stream has synchronised. */
 typedef enum {
@@ -147,7 +155,9 @@ typedef enum {
   MONO_T_SHARED = 11,  /* [R][H] act */
   MONO_T_ROUTED = 12,  /* [R][H] f32 */
   MONO_T_BLOCK = 13,   /* [R][H] act */
-  MONO_T_CARRY = 14    /* [R][25] f32 */
+  MONO_T_CARRY = 14,   /* [R][25] f32 */
+  MONO_T_TRACE = 15    /* [grid][32] uint64: per-workgroup phase timestamps of the last traced
+                          mono_ffn_layer (100 MHz real-time counter), see mono_workspace_set_trace */
 } mono_tensor;
 
 /* Device address and size of one intermediate inside ws (host-side arithmetic only). */

@@ -20,10 +20,10 @@ FMT = {"f32": MONO_F32, "bf16": MONO_BF16, "q8_0": MONO_Q8_0, "mxfp4": MONO_MXFP
 MONO_OK, MONO_E_INVAL, MONO_E_UNSUPPORTED, MONO_E_DEVICE, MONO_E_TIMEOUT = 0, -1, -2, -3, -4
 (MONO_T_MIXES, MONO_T_PRE, MONO_T_POST, MONO_T_COMB, MONO_T_X, MONO_T_NORM, MONO_T_LOGITS,
  MONO_T_IDX, MONO_T_WEIGHTS, MONO_T_H_ROUTED, MONO_T_H_SHARED, MONO_T_SHARED, MONO_T_ROUTED,
- MONO_T_BLOCK, MONO_T_CARRY) = range(15)
+ MONO_T_BLOCK, MONO_T_CARRY, MONO_T_TRACE) = range(16)
 
 EXPORTS = ("mono_workspace_bytes", "mono_workspace_init", "mono_workspace_poll",
-           "mono_workspace_set_debug", "mono_workspace_tensor", "mono_last_error",
+           "mono_workspace_set_debug", "mono_workspace_set_trace", "mono_workspace_tensor", "mono_last_error",
            "mono_grid_size", "mono_hc_mix_collapse", "mono_router_select", "mono_moe_experts",
            "mono_hc_expand", "mono_ffn_layer")
 
@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
             "mono_workspace_init": (I, [P, SP, P]),
             "mono_workspace_poll": (I, [P, ctypes.POINTER(ctypes.c_uint32), P]),
             "mono_workspace_set_debug": (I, [P, ctypes.c_uint32, ctypes.c_int32, ctypes.c_int32, P]),
+            "mono_workspace_set_trace": (I, [P, I, P]),
             "mono_workspace_tensor": (I, [SP, P, I, ctypes.POINTER(ctypes.c_void_p),
                                           ctypes.POINTER(ctypes.c_size_t)]),
             "mono_last_error": (ctypes.c_char_p, []),
@@ -147,6 +148,10 @@ def mono_workspace_init(ws, shape: Shape, stream=None) -> None:
 def mono_workspace_set_debug(ws, spin_limit_ticks=0, fault_wg=-1, fault_phase=0,
                              stream=None) -> None:
     _ok(lib().mono_workspace_set_debug(ptr(ws), spin_limit_ticks, fault_wg, fault_phase, stream))
+
+
+def mono_workspace_set_trace(ws, enable=True, stream=None) -> None:
+    _ok(lib().mono_workspace_set_trace(ptr(ws), 1 if enable else 0, stream))
 
 
 def mono_workspace_poll(ws, stream=None):

@@ -19,6 +19,7 @@
 
 namespace mono {
 int launch_debug(uint32_t* ctl, uint32_t spin, uint32_t fwg, uint32_t fph, void* stream);
+int launch_trace(uint32_t* ctl, uint32_t on, void* stream);
 }
 
 using namespace mono;
@@ -86,6 +87,11 @@ void check_shape(Check& c, const mono_shape* s) {
     if ((size_t)s->rows * wide * ab > (size_t)kLdsHidBytes)
       c.fail(MONO_E_UNSUPPORTED, "rows*max(inter, shared_inter)*%zu exceeds the %d-byte hidden-row buffer",
              ab, kLdsHidBytes);
+    if (wide * ab > 16384)
+      c.fail(MONO_E_UNSUPPORTED, "max(inter, shared_inter)*%zu exceeds 16384 bytes per hidden row", ab);
+    if ((size_t)(s->rows + 1) * s->hidden * ab > (size_t)kLdsActBytes)
+      c.fail(MONO_E_UNSUPPORTED, "(rows + 1)*hidden*%zu exceeds the %d-byte activation buffer", ab,
+             kLdsActBytes);
   }
 }
 
@@ -179,6 +185,7 @@ Params base_params(const mono_shape* s, const mono_layer* L, void* ws, int grid)
   p.ctl = reinterpret_cast<uint32_t*>(b + W.ctl);
   p.mix_part = reinterpret_cast<float*>(b + W.mix_part);
   p.carry_part = reinterpret_cast<float*>(b + W.carry_part);
+  p.trace = reinterpret_cast<uint64_t*>(b + W.trace);
   p.h_routed = b + W.h_routed;
   p.h_shared = b + W.h_shared;
   return p;
@@ -251,6 +258,19 @@ mono_status mono_workspace_set_debug(void* ws, uint32_t spin_limit_ticks, int32_
   return MONO_OK;
 }
 
+mono_status mono_workspace_set_trace(void* ws, int enable, void* stream) {
+  Check c;
+  c.ptr(ws, "ws", 256);
+  if (c.code != MONO_OK) return c.done();
+  const int rc = launch_trace(static_cast<uint32_t*>(ws), enable ? 1u : 0u, stream);
+  if (rc != 0) {
+    g_error = std::string("set_trace: ") + hipGetErrorString((hipError_t)rc);
+    return MONO_E_DEVICE;
+  }
+  g_error.clear();
+  return MONO_OK;
+}
+
 mono_status mono_workspace_poll(const void* ws, uint32_t err[4], void* stream) {
   Check c;
   c.ptr(ws, "ws", 256);
@@ -293,6 +313,7 @@ mono_status mono_workspace_tensor(const mono_shape* shape, void* ws, mono_tensor
     case MONO_T_ROUTED: off = W.routed; n = R * H * 4; break;
     case MONO_T_BLOCK: off = W.block; n = R * H * ab; break;
     case MONO_T_CARRY: off = W.carry; n = R * kNCarry * 4; break;
+    case MONO_T_TRACE: off = W.trace; n = (size_t)kMaxGrid * kTraceSlots * 8; break;
     default:
       c.fail(MONO_E_INVAL, "unknown tensor %d", (int)which);
       return c.done();

@@ -16,7 +16,7 @@ constexpr int kBlock = 512;          /* threads per workgroup, every kernel */
 constexpr int kWaves = kBlock / 64;  /* wave64 */
 constexpr int kMaxRows = 8;
 constexpr int kMaxTopK = 16;
-constexpr int kMaxExperts = 1024;
+constexpr int kMaxExperts = 512;
 constexpr int kNMix = 24;            /* 4 pre + 4 post + 16 comb */
 constexpr int kNCarry = kNMix + 1;   /* raw mix sums + sum of squares */
 constexpr int kMixChunk = 256;       /* flattened HC-row elements per mix partial */
@@ -34,11 +34,15 @@ enum {
   CTL_SPIN = 16,     /* bounded-wait limit in real-time ticks (0 = default) */
   CTL_FAULT_WG = 17, /* workgroup that skips a barrier arrival (-1 = none) */
   CTL_FAULT_PHASE = 18,
-  CTL_WORDS = 64
+  CTL_TRACE = 19,    /* nonzero: the fused launch records per-phase timestamps */
+  CTL_XEND64 = 60,   /* uint64 arrival counter of the unfused expand (last-arriver election) */
+  CTL_BAR64 = 64,    /* 4 barriers x 8 groups of uint64 arrival counters, never reset */
+  CTL_WORDS = 128
 };
 
 /* Barrier phases (also reported in the error word). */
-enum { PH_MIX = 1, PH_ROUTER = 2, PH_GATEUP = 3, PH_CARRY = 4 };
+enum { PH_MIX = 1, PH_ROUTER = 2, PH_GATEUP = 3, PH_END = 4 };
+constexpr int kBarGroups = 8; /* one arrival counter per group of workgroups (blockIdx % 8) */
 
 struct Mat {
   int fmt;
@@ -94,13 +98,14 @@ struct Params {
   /* workspace scratch */
   float* mix_part;   /* [nchunk][R][25] */
   float* carry_part; /* [nslice][R][25] */
+  uint64_t* trace;   /* [grid][16] real-time stamps */
   uint32_t* ctl;
 };
 
 /* Workspace layout (byte offsets, 256-byte aligned regions). */
 struct WsLayout {
   size_t ctl, mix_part, carry_part, mixes, pre, post, comb, x, norm, logits, idx, weights,
-      h_routed, h_shared, shared, routed, block, carry, total;
+      h_routed, h_shared, shared, routed, block, carry, trace, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -135,6 +140,7 @@ inline WsLayout ws_layout(const mono_shape& s) {
   L.routed = take(R * H * 4);
   L.block = take(R * H * ab);
   L.carry = take(R * kNCarry * 4);
+  L.trace = take((size_t)kMaxGrid * 16 * 8);
   L.total = o;
   return L;
 }
@@ -152,6 +158,7 @@ enum Kernel {
   K_WS_INIT,
   K_WS_DEBUG
 };
+constexpr int kTraceSlots = 32;
 int launch(Kernel k, const Params& p, int act, int rfmt, int sfmt, int grid, void* stream);
 int grid_size_for_device(int device);
 int max_active_persistent(int act, int rfmt, int sfmt, int rows);

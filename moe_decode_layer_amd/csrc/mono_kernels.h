@@ -1,0 +1,1629 @@
+/*
+ * libmonolayer device code for gfx950 (CDNA4, wave64): phases, kernels and launch templates.
+ * Included by the per-format translation units; nothing here is instantiated on its own.
+ *
+ * The layer-half step is written as phases (device functions). The unfused entry points run
+ * each phase as its own kernel; the fused entry point runs every phase in ONE persistent launch
+ * (one workgroup per compute unit) separated by device-wide barriers. Every output element has
+ * a fixed decomposition (one wave per dot product, fixed lane mapping, fixed reduction tree),
+ * independent of which workgroup computes it, so the fused and unfused paths give identical
+ * bytes.
+ *
+ * The step is a chain of HBM-bound matrix-vector products (1 to 8 activation rows against
+ * weights read once), so it runs on the vector ALUs: each lane streams 16-byte weight vectors
+ * (1 KB per wave per step, coalesced), a wave keeps a whole row's loads in flight, weights are
+ * decoded once per vector into packed bf16 pairs (exact for bf16, Q8_0 and e2m1 values) and
+ * every activation row consumes them with v_dot2_f32_bf16 (exact products, f32 sums).
+ * Activations live in LDS. Reductions use DPP. MFMA is not used at these widths.
+ *
+ * Data that crosses workgroups inside the fused launch (mix partials, logits, hidden rows,
+ * carry partials) is written with device-coherent (sc1) stores and read with device-coherent
+ * loads; a barrier is a plain device-scope counter that a workgroup increments only after its
+ * stores have completed. No cache write-back or invalidation is needed.
+ *
+ * Steps and rounding points follow the ds4 page "v41: fuse the single-box decode glue (HC, MoE,
+ * attention)" ("What" and its HC and router/shared-expert commits); the fused launch follows K2
+ * of the SGLang page "[AMD][V4.1] Mono kernel framework ... DeepSeek-V4.1 decode layers" (figure
+ * "DeepSeek-V4.1 layer on mono"), the load order of the lm-sys page "Add the AMD low-latency
+ * kernels section" (Layer diagram: mHC mix weights and the shared expert early, routed experts
+ * after routing) and the post -> next-pre carry of the SGLang page "[DeepSeek-V4] Add
+ * mhc_fused_post_pre kernel" ("Motivation").
+ */
+#ifndef MONOLAYER_KERNELS_H
+#define MONOLAYER_KERNELS_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mono_internal.h"
+
+namespace mono {
+
+enum { F32 = MONO_F32, BF16 = MONO_BF16, Q8 = MONO_Q8_0, FP4 = MONO_MXFP4 };
+
+constexpr int kMaxUnion = kMaxRows * kMaxTopK;
+constexpr int kRG = 4; /* consecutive down-projection rows per task */
+constexpr int kMaxStaged = 160; /* hidden rows staged at once (80 KB / 512 B at least) */
+constexpr uint32_t kHidShared = 0x80000000u;
+
+/* ------------------------------------------------------------------------------------------
+ * Number formats */
+
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+/* f32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32). */
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+/* Two f32 -> packed bf16 pair (lo in the low half), round to nearest even. */
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int ACT>
+__device__ __forceinline__ float act_round(float v) {
+  return ACT == F32 ? v : bf2f(f2bf(v));
+}
+
+template <int ACT>
+__device__ __forceinline__ float act_ld(const void* p, size_t i) {
+  if (ACT == F32) return static_cast<const float*>(p)[i];
+  return bf2f(static_cast<const uint16_t*>(p)[i]);
+}
+
+/* Stores v (already rounded to the act type). */
+template <int ACT>
+__device__ __forceinline__ void act_st(void* p, size_t i, float v) {
+  if (ACT == F32)
+    static_cast<float*>(p)[i] = v;
+  else
+    static_cast<uint16_t*>(p)[i] = (uint16_t)f2bf(v);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+/* e8m0 scale 2^(e-127). */
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  if (e == 0) return __uint_as_float(0x00400000u);
+  if (e == 255) return __uint_as_float(0x7FC00000u);
+  return __uint_as_float(e << 23);
+}
+
+/* c + a.lo * b.lo + a.hi * b.hi for packed bf16 pairs. */
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Device-coherent accesses for data shared between workgroups of one launch */
+
+template <typename T>
+__device__ __forceinline__ T ld_coh(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st_coh(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ldf_coh(const float* p) {
+  return __uint_as_float(ld_coh(reinterpret_cast<const uint32_t*>(p)));
+}
+__device__ __forceinline__ void stf_coh(float* p, float v) {
+  st_coh(reinterpret_cast<uint32_t*>(p), __float_as_uint(v));
+}
+template <int ACT>
+__device__ __forceinline__ void act_st_coh(void* p, size_t i, float v) {
+  if (ACT == F32)
+    stf_coh(static_cast<float*>(p) + i, v);
+  else
+    st_coh(static_cast<uint16_t*>(p) + i, (uint16_t)f2bf(v));
+}
+
+/* Device-coherent (sc1) loads issued as buffer loads: unlike atomic loads they are ordinary
+ * memory operations, so a wave keeps many in flight. Offsets are bytes inside the region the
+ * resource covers; reads past its end return 0. */
+typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u_t __attribute__((ext_vector_type(2)));
+constexpr int kCohPolicy = 16; /* sc1: device scope */
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_region(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ float coh_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCohPolicy));
+}
+__device__ __forceinline__ uint4 coh_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCohPolicy);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+/* Waits until this wave's memory operations have completed (and orders the compiler). */
+__device__ __forceinline__ void drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+/* ------------------------------------------------------------------------------------------
+ * Wave reductions (DPP butterflies inside each row of 16 lanes, then the four row sums). Must
+ * be called with all 64 lanes active; every lane returns the same value. */
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ float readlane(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<0xB1>(v);  /* quad_perm [1,0,3,2] */
+  v += dpp<0x4E>(v);  /* quad_perm [2,3,0,1] */
+  v += dpp<0x141>(v); /* row_half_mirror */
+  v += dpp<0x140>(v); /* row_mirror */
+  return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Weight streaming. A step of a row covers 64 lanes x 16 bytes (1 KB): 4 f32, 8 bf16, 16 Q8_0
+ * or 32 MXFP4 values per lane, so lane L of step s holds elements [(64 s + L) * EL, + EL).
+ * CH_GU / CH_DN: steps a wave keeps in flight per row in the gate/up and down phases. */
+
+template <int FMT> struct Fmt;
+template <> struct Fmt<F32> { static constexpr int EL = 4, CH_GU = 8, CH_DN = 4, PAIRS = 0; };
+template <> struct Fmt<BF16> { static constexpr int EL = 8, CH_GU = 10, CH_DN = 4, PAIRS = 4; };
+template <> struct Fmt<Q8> { static constexpr int EL = 16, CH_GU = 5, CH_DN = 2, PAIRS = 8; };
+template <> struct Fmt<FP4> { static constexpr int EL = 32, CH_GU = 3, CH_DN = 1, PAIRS = 16; };
+
+__host__ __device__ constexpr size_t row_vbytes(int fmt, size_t k) {
+  return fmt == F32 ? 4 * k : fmt == BF16 ? 2 * k : fmt == Q8 ? k : k / 2;
+}
+__host__ __device__ constexpr size_t row_sbytes(int fmt, size_t k) {
+  return fmt == Q8 ? (k / 32) * 2 : fmt == FP4 ? k / 32 : 0;
+}
+
+template <int FMT>
+__device__ __forceinline__ void wload(const uint8_t* vrow, const uint8_t* srow, int s, int lane,
+                                      int K, uint4& v, uint32_t& sc) {
+  const int q = s * 64 + lane;
+  const int k = q * Fmt<FMT>::EL;
+  if (k < K) {
+    v = *reinterpret_cast<const uint4*>(vrow + (size_t)q * 16);
+    if (FMT == Q8) sc = *reinterpret_cast<const uint16_t*>(srow + (k / 32) * 2);
+    if (FMT == FP4) sc = srow[k / 32];
+  } else {
+    v = make_uint4(0, 0, 0, 0);
+    sc = 0;
+  }
+}
+
+/* Exact decode of one 16-byte weight vector into packed bf16 pairs (element 2m in the low
+ * half of pair m) and its block scale. Q8_0: each int8 q becomes f32 through the unsigned byte
+ * q ^ 0x80 minus 128, whose top 16 bits are the exact bf16 of q. MXFP4: each byte converts to
+ * a bf16 pair (low nibble first) with unit scale; the e8m0 scale multiplies the partial sum. */
+template <int FMT>
+__device__ __forceinline__ void decode(const uint4& v, uint32_t sc, uint32_t (&w)[Fmt<FMT>::PAIRS],
+                                       float& scale) {
+  if constexpr (FMT == BF16) {
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    scale = 1.0f;
+  } else if constexpr (FMT == Q8) {
+    const uint32_t d[4] = {v.x ^ 0x80808080u, v.y ^ 0x80808080u, v.z ^ 0x80808080u,
+                           v.w ^ 0x80808080u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float f0 = (float)(d[i] & 0xFFu) - 128.0f;
+      const float f1 = (float)((d[i] >> 8) & 0xFFu) - 128.0f;
+      const float f2 = (float)((d[i] >> 16) & 0xFFu) - 128.0f;
+      const float f3 = (float)(d[i] >> 24) - 128.0f;
+      w[2 * i] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+      w[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+    }
+    scale = f16_to_f32(sc);
+  } else if constexpr (FMT == FP4) {
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], 1.0f, 0));
+      w[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], 1.0f, 1));
+      w[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], 1.0f, 2));
+      w[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], 1.0f, 3));
+    }
+    scale = e8m0_to_f32(sc);
+  }
+}
+
+/* acc + scale * (pairs . bf16 activations k .. k + 2 PAIRS - 1 of one LDS row). */
+template <int FMT>
+__device__ __forceinline__ float dot_pairs(const uint32_t (&w)[Fmt<FMT>::PAIRS], float scale,
+                                           const void* arow, int k, float acc) {
+  constexpr int P = Fmt<FMT>::PAIRS;
+  const uint16_t* a = static_cast<const uint16_t*>(arow) + k;
+  if constexpr (FMT == BF16) {
+    const uint4 x = *reinterpret_cast<const uint4*>(a);
+    acc = dot2bf(w[0], x.x, acc);
+    acc = dot2bf(w[1], x.y, acc);
+    acc = dot2bf(w[2], x.z, acc);
+    acc = dot2bf(w[3], x.w, acc);
+    return acc;
+  } else {
+    float part = 0.0f;
+#pragma unroll
+    for (int c = 0; c < P / 4; ++c) {
+      const uint4 x = *reinterpret_cast<const uint4*>(a + 8 * c);
+      part = dot2bf(w[4 * c + 0], x.x, part);
+      part = dot2bf(w[4 * c + 1], x.y, part);
+      part = dot2bf(w[4 * c + 2], x.z, part);
+      part = dot2bf(w[4 * c + 3], x.w, part);
+    }
+    return fmaf(scale, part, acc);
+  }
+}
+
+/* f32 weights against f32 activations (the all-f32 workload). */
+__device__ __forceinline__ float dot_f32(const uint4& v, const void* arow, int k, float acc) {
+  const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(arow) + k);
+  acc = fmaf(__uint_as_float(v.x), x.x, acc);
+  acc = fmaf(__uint_as_float(v.y), x.y, acc);
+  acc = fmaf(__uint_as_float(v.z), x.z, acc);
+  acc = fmaf(__uint_as_float(v.w), x.w, acc);
+  return acc;
+}
+
+/* Weight registers of CH steps of NR rows (one chunk of a wave task). */
+template <int FMT, int NR, int CH>
+struct WRegs {
+  uint4 v[NR][CH];
+  uint32_t sc[NR][CH];
+};
+
+template <int FMT, int NR, int CH>
+__device__ __forceinline__ void wregs_load(WRegs<FMT, NR, CH>& W, const uint8_t* const (&vrow)[NR],
+                                           const uint8_t* const (&srow)[NR], int K, int s0) {
+  constexpr int EL = Fmt<FMT>::EL;
+  const int lane = threadIdx.x & 63;
+  const int nsteps = (K + 64 * EL - 1) / (64 * EL);
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+      if (s0 + c < nsteps) {
+        wload<FMT>(vrow[m], srow[m], s0 + c, lane, K, W.v[m][c], W.sc[m][c]);
+      } else {
+        W.v[m][c] = make_uint4(0, 0, 0, 0);
+        W.sc[m][c] = 0;
+      }
+    }
+}
+
+/* acc[m][r] += (chunk of row m) . act_r for every r in `mask` (per-lane partials). */
+template <int FMT, int ACT, int RMAX, int NR, int CH>
+__device__ __forceinline__ void wregs_dot(const WRegs<FMT, NR, CH>& W, int K, int s0,
+                                          const void* const (&arow)[RMAX], uint32_t mask,
+                                          float (&acc)[NR][RMAX]) {
+  constexpr int EL = Fmt<FMT>::EL;
+  const int lane = threadIdx.x & 63;
+  const int nsteps = (K + 64 * EL - 1) / (64 * EL);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int k = ((s0 + c) * 64 + lane) * EL;
+    if (s0 + c < nsteps && k < K) {
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        if constexpr (FMT == F32) {
+#pragma unroll
+          for (int r = 0; r < RMAX; ++r)
+            if (mask & (1u << r)) acc[m][r] = dot_f32(W.v[m][c], arow[r], k, acc[m][r]);
+        } else {
+          uint32_t w[Fmt<FMT>::PAIRS];
+          float scale;
+          decode<FMT>(W.v[m][c], W.sc[m][c], w, scale);
+#pragma unroll
+          for (int r = 0; r < RMAX; ++r)
+            if (mask & (1u << r)) acc[m][r] = dot_pairs<FMT>(w, scale, arow[r], k, acc[m][r]);
+        }
+      }
+    }
+  }
+}
+
+/* acc[m][r] += row_m . act_r over K elements, CH steps of all NR rows in flight at a time. */
+template <int FMT, int ACT, int RMAX, int NR, int CH>
+__device__ __forceinline__ void dot_rows(const uint8_t* const (&vrow)[NR],
+                                         const uint8_t* const (&srow)[NR], int K,
+                                         const void* const (&arow)[RMAX], uint32_t mask,
+                                         float (&acc)[NR][RMAX], int s_begin = 0) {
+  constexpr int EL = Fmt<FMT>::EL;
+  const int nsteps = (K + 64 * EL - 1) / (64 * EL);
+  for (int s0 = s_begin; s0 < nsteps; s0 += CH) {
+    WRegs<FMT, NR, CH> W;
+    wregs_load(W, vrow, srow, K, s0);
+    wregs_dot<FMT, ACT, RMAX, NR, CH>(W, K, s0, arow, mask, acc);
+  }
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Workgroup shared memory */
+
+struct Smem {
+  alignas(16) uint8_t big[kLdsActBytes]; /* act rows [R][H] + norm weight [H]; down phase:
+                                            staged hidden rows, then y and block values */
+  float raw[kMaxRows][kNCarry];
+  float mixes[kMaxRows][kNMix];
+  float pre[kMaxRows][4];
+  float post[kMaxRows][4];
+  float comb[kMaxRows][16];
+  float hcs[4];
+  float hcb[kNMix];
+  float red[kWaves][kMaxRows];
+  float rsum[kMaxRows];
+  int sel_e[kMaxRows][kMaxTopK];
+  float sel_s[kMaxRows][kMaxTopK];
+  float sel_w[kMaxRows][kMaxTopK];
+  int U[kMaxUnion + 1];
+  uint32_t umask[kMaxUnion + 1];
+  int8_t uslot[kMaxUnion + 1][kMaxRows];
+  uint16_t voff[kMaxUnion + 1][kMaxRows]; /* staged hidden row offset per (item, row), 16 B */
+  uint8_t used[kMaxExperts];
+  uint32_t vsrc[kMaxStaged]; /* staged hidden rows: source offset (flag: shared), */
+  uint16_t vdst[kMaxStaged]; /* LDS offset in 16 B, */
+  uint16_t vlen[kMaxStaged]; /* length in 16 B */
+  int nv;
+  int nU;
+  int flag;
+  uint64_t epoch;
+  int trace_on;
+  int state_in_lds;
+  float bias[kMaxExperts];
+  uint32_t spin;
+  int skip_phase;
+};
+
+/* ------------------------------------------------------------------------------------------
+ * Device-wide barriers, split into arrive and wait so that independent work can run between
+ * them. Each barrier has a 64-bit arrival counter that is never reset: a workgroup completes
+ * its stores, then adds 1 (no return value needed). At launch start every workgroup reads the
+ * counters; since a barrier cannot complete before every workgroup has arrived, the count it
+ * reads is below (epoch + 1) * grid for the epoch of this launch, so epoch = count / grid and
+ * the barrier completes when the count reaches (epoch + 1) * grid. Waits are bounded: on
+ * expiry the error word is set and every thread of the workgroup gets false (the workspace then
+ * needs mono_workspace_init). Fault injection: workgroup fault_wg skips its arrival at
+ * fault_phase. */
+
+/* Counter of `group` for barrier `phase`. Workgroup w arrives on group w % 8, so 32 (not 256)
+ * arrivals contend for one address; a waiter reads the 8 counters in parallel. */
+__device__ __forceinline__ uint64_t* bar_counter(const Params& p, int phase, int group) {
+  return reinterpret_cast<uint64_t*>(p.ctl + CTL_BAR64) + (phase - 1) * kBarGroups + group;
+}
+
+__device__ __forceinline__ void report_timeout(const Params& p, int phase) {
+  uint32_t* e = p.ctl + CTL_ERR;
+  if (atomicCAS(&e[0], 0u, 1u) == 0u) {
+    st_coh(&e[1], (uint32_t)phase);
+    st_coh(&e[2], (uint32_t)blockIdx.x);
+  }
+  atomicAdd(&e[3], 1u);
+}
+
+/* Reads the launch epoch and debug words once per launch (made visible to the workgroup by the
+ * next __syncthreads). Every fused launch advances every barrier counter of group g by exactly
+ * n_g = ceil((grid - g) / 8) (a launch given a carry still arrives at the mix barrier), and the
+ * end counters advance only after every workgroup has passed the gate/up barrier, hence after
+ * every workgroup has started and read them here. So at launch start each end counter holds
+ * epoch * n_g exactly, and every barrier of this launch completes when each group counter
+ * reaches (epoch + 1) * n_g. */
+__device__ __forceinline__ void bar_setup(const Params& p, Smem& sm) {
+  if (threadIdx.x == 0) {
+    sm.trace_on = ld_coh(p.ctl + CTL_TRACE) != 0u;
+    const uint64_t n0 = ((uint64_t)gridDim.x + kBarGroups - 1) / kBarGroups;
+    const uint64_t epoch = ld_coh(bar_counter(p, PH_END, 0)) / n0;
+    sm.epoch = epoch;
+    const uint32_t spin = ld_coh(p.ctl + CTL_SPIN);
+    const uint32_t fwg = ld_coh(p.ctl + CTL_FAULT_WG), fph = ld_coh(p.ctl + CTL_FAULT_PHASE);
+    sm.spin = spin ? spin : kDefaultSpin;
+    sm.skip_phase = (int32_t)fwg == (int32_t)blockIdx.x ? (int)fph : -1;
+  }
+}
+
+__device__ __forceinline__ uint64_t bar_target(const Smem& sm, int g) {
+  const uint64_t n = ((uint64_t)gridDim.x - g + kBarGroups - 1) / kBarGroups;
+  return (sm.epoch + 1) * n;
+}
+
+__device__ __forceinline__ void bar_arrive(const Params& p, Smem& sm, int phase) {
+  drain();
+  __syncthreads();
+  if (threadIdx.x == 0 && sm.skip_phase != phase)
+    __hip_atomic_fetch_add(bar_counter(p, phase, blockIdx.x % kBarGroups), (uint64_t)1,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool bar_wait(const Params& p, Smem& sm, int phase) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int g = lane < kBarGroups ? lane : 0;
+    const uint64_t* cnt = bar_counter(p, phase, g);
+    const uint64_t target = bar_target(sm, g);
+    int ok = 1;
+    if (__ballot(lane < kBarGroups && ld_coh(cnt) < target) != 0ull) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__ballot(lane < kBarGroups && ld_coh(cnt) < target) != 0ull) {
+        __builtin_amdgcn_s_sleep(1);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > sm.spin) {
+          if (lane == 0) report_timeout(p, phase);
+          ok = 0;
+          break;
+        }
+      }
+    }
+    if (lane == 0) sm.flag = ok;
+  }
+  __syncthreads();
+  return sm.flag != 0;
+}
+
+/* Arrival at the end counters (every workgroup of every fused launch arrives once) that tells
+ * the caller whether this workgroup may sum the carry partials: it completed its own group and
+ * then found every other group complete. The last increment overall always qualifies; if two
+ * qualify they write identical values. All threads get the answer. */
+__device__ __forceinline__ bool arrive_last(const Params& p, Smem& sm) {
+  drain();
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int mine = blockIdx.x % kBarGroups;
+    uint64_t v = 0;
+    if (lane == 0)
+      v = __hip_atomic_fetch_add(bar_counter(p, PH_END, mine), (uint64_t)1, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT) + 1;
+    const uint64_t mine_now = __shfl(v, 0);
+    const int g = lane < kBarGroups ? lane : 0;
+    uint64_t c = 0;
+    if (lane < kBarGroups && lane != mine) c = ld_coh(bar_counter(p, PH_END, g));
+    if (lane == mine) c = mine_now;
+    const bool done = lane >= kBarGroups || c >= bar_target(sm, g);
+    const bool all = __ballot(!done) == 0ull;
+    const bool own_last = mine_now == bar_target(sm, mine);
+    if (lane == 0) sm.flag = (all && own_last) ? 1 : 0;
+  }
+  __syncthreads();
+  return sm.flag != 0;
+}
+
+/* Last-arriver election of a plain (non-persistent) launch: one counter that every launch
+ * advances by exactly its grid size, so the arrival that makes it a multiple of the grid size
+ * is the last of this launch. All threads get the answer. */
+__device__ __forceinline__ bool arrive_last_single(const Params& p, Smem& sm) {
+  drain();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint64_t a = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(p.ctl + CTL_XEND64),
+                                              (uint64_t)1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    sm.flag = ((a + 1) % gridDim.x) == 0 ? 1 : 0;
+  }
+  __syncthreads();
+  return sm.flag != 0;
+}
+
+__device__ __forceinline__ void stamp(const Params& p, bool on, int slot) {
+  if (on && threadIdx.x == 0)
+    p.trace[(size_t)blockIdx.x * kTraceSlots + slot] = __builtin_amdgcn_s_memrealtime();
+}
+
+/* Task order for phases with fewer tasks than waves: consecutive tasks go to different compute
+ * units first (task t -> workgroup t % G, wave t / G). */
+__device__ __forceinline__ int wave_major_id() {
+  return (threadIdx.x >> 6) * gridDim.x + blockIdx.x;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Phase: mix partials [ds4 HC fusion commit: rms_norm_mix over the 4 x H row; SGLang fused
+ * post/pre page: pre-norm GEMM partials + RMS square-sum partials]. Chunk t (256 consecutive
+ * elements of the flattened row) is one wave task: part[t][r][j] = W_mix[j] . s over the chunk,
+ * part[t][r][24] = sum s^2 over the chunk. */
+template <int ACT, int RMAX>
+__device__ __forceinline__ void ph_mix_partials(const Params& p) {
+  const int n = 4 * p.H, nch = n / kMixChunk;
+  const int lane = threadIdx.x & 63;
+  const int nwt = gridDim.x * kWaves;
+  /* task = (chunk, row), so each wave reduces 25 sums whatever the number of rows */
+  for (int t = wave_major_id(); t < nch * p.R; t += nwt) {
+    const int ch = t / p.R, r = t % p.R;
+    const int base = ch * kMixChunk + lane * 4;
+    float4 w[kNMix];
+#pragma unroll
+    for (int j = 0; j < kNMix; ++j)
+      w[j] = *reinterpret_cast<const float4*>(p.w_mix + (size_t)j * n + base);
+    float s[4];
+    if (ACT == F32) {
+      const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(p.state) +
+                                                        (size_t)r * n + base);
+      s[0] = v.x; s[1] = v.y; s[2] = v.z; s[3] = v.w;
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.state) +
+                                                      (size_t)r * n + base);
+      s[0] = bf2f(v.x & 0xFFFFu); s[1] = bf2f(v.x >> 16);
+      s[2] = bf2f(v.y & 0xFFFFu); s[3] = bf2f(v.y >> 16);
+    }
+    float* out = p.mix_part + ((size_t)ch * p.R + r) * kNCarry;
+#pragma unroll
+    for (int j = 0; j < kNMix; ++j) {
+      float a = w[j].x * s[0];
+      a = fmaf(w[j].y, s[1], a);
+      a = fmaf(w[j].z, s[2], a);
+      a = fmaf(w[j].w, s[3], a);
+      const float tot = wave_sum(a);
+      if (lane == 0) stf_coh(out + j, tot);
+    }
+    float ss = s[0] * s[0];
+    ss = fmaf(s[1], s[1], ss);
+    ss = fmaf(s[2], s[2], ss);
+    ss = fmaf(s[3], s[3], ss);
+    const float tot = wave_sum(ss);
+    if (lane == 0) stf_coh(out + kNMix, tot);
+  }
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Prologue of the pre side: hc parameters and the norm weight into LDS (the norm weight sits
+ * after the R activation rows in sm.big). */
+template <int ACT>
+__device__ __forceinline__ void load_pre_params(const Params& p, Smem& sm) {
+  const int tid = threadIdx.x;
+  if (tid < 3) sm.hcs[tid] = p.hc_scale[tid];
+  if (tid < kNMix) sm.hcb[tid] = p.hc_base[tid];
+  const size_t ab = ACT == F32 ? 4 : 2;
+  const size_t rows = (size_t)p.R * p.H * ab, wbytes = (size_t)p.H * ab;
+  const uint4* s = static_cast<const uint4*>(p.w_norm);
+  uint4* d = reinterpret_cast<uint4*>(sm.big + rows);
+  for (size_t i = tid; i < wbytes / 16; i += kBlock) d[i] = s[i];
+  /* the state rows too when they fit after the norm weight (one row does: 40 KB at H 5120) */
+  const size_t sbytes = 4 * rows;
+  const bool fits = rows + wbytes + sbytes <= (size_t)kLdsActBytes;
+  if (fits) {
+    const uint4* ss = static_cast<const uint4*>(p.state);
+    uint4* sd = reinterpret_cast<uint4*>(sm.big + rows + wbytes);
+    for (size_t i = tid; i < sbytes / 16; i += kBlock) sd[i] = ss[i];
+  }
+  if (tid == 0) sm.state_in_lds = fits ? 1 : 0;
+}
+
+/* Router bias into LDS (read by the select of every workgroup). */
+__device__ __forceinline__ void load_bias(const Params& p, Smem& sm) {
+  for (int e = threadIdx.x; e < p.E; e += kBlock) sm.bias[e] = p.bias[e];
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Phase: mHC pre side for all rows, run by one whole workgroup (redundantly by every
+ * workgroup of the fused launch): mixes from the partials (or the carry); split / Sinkhorn;
+ * collapse; weighted RMSNorm. The norm rows are left in sm.big as act values.
+ * READING (mHC, not on the pages): pre = sigmoid(a0 m[i] + b[i]); post = 2 sigmoid(a1 m[4+i]
+ * + b[4+i]); comb = Sinkhorn on exp(a2 m[8+4i+j] + b[8+4i+j] - max), rows then columns.
+ * Needs load_pre_params first (and a __syncthreads between). */
+template <int ACT, int RMAX>
+__device__ __forceinline__ void ph_hc_pre(const Params& p, Smem& sm, bool write_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = p.R, H = p.H, n = 4 * H, nch = n / kMixChunk;
+  constexpr int VE = ACT == F32 ? 4 : 8; /* elements per 16-byte state load */
+  const size_t ab = ACT == F32 ? 4 : 2;
+  /* raw mix sums: one wave per (row, output); lanes take chunks t = lane + 64 m; the loads of
+   * up to 8 sums are issued before any is reduced */
+  constexpr int PB = 8;
+  const __amdgpu_buffer_rsrc_t part = coh_region(p.mix_part, (size_t)nch * R * kNCarry * 4);
+  for (int q0 = wave; q0 < R * kNCarry; q0 += kWaves * PB) {
+    float v[PB];
+#pragma unroll
+    for (int b = 0; b < PB; ++b) v[b] = 0.0f;
+    for (int t0 = 0; t0 < nch; t0 += 64) {
+      const int t = t0 + lane;
+#pragma unroll
+      for (int b = 0; b < PB; ++b) {
+        const int q = q0 + b * kWaves;
+        if (q < R * kNCarry) {
+          const int r = q / kNCarry, j = q % kNCarry;
+          if (p.carry_in) {
+            if (t == 0) v[b] += p.carry_in[r * kNCarry + j];
+          } else if (t < nch) {
+            v[b] += coh_f32(part, (uint32_t)((((size_t)t * R + r) * kNCarry + j) * 4));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < PB; ++b) {
+      const int q = q0 + b * kWaves;
+      if (q < R * kNCarry) {
+        const float tot = wave_sum(v[b]);
+        if (lane == 0) sm.raw[q / kNCarry][q % kNCarry] = tot;
+      }
+    }
+  }
+  __syncthreads();
+  stamp(p, sm.trace_on != 0, 14);
+  if (tid < R * kNMix) {
+    const int r = tid / kNMix, j = tid % kNMix;
+    const float den = sqrtf(sm.raw[r][kNMix] / (float)n + p.eps_hc);
+    const float m = sm.raw[r][j] / den;
+    sm.mixes[r][j] = m;
+    if (write_out && p.mixes) p.mixes[r * kNMix + j] = m;
+  }
+  __syncthreads();
+  stamp(p, sm.trace_on != 0, 15);
+  /* pre / post gates: one thread each */
+  if (tid < R * 8) {
+    const int r = tid >> 3, g = tid & 7;
+    const float* m = sm.mixes[r];
+    if (g < 4) {
+      const float v = 1.0f / (1.0f + expf(-(sm.hcs[0] * m[g] + sm.hcb[g])));
+      sm.pre[r][g] = v;
+      if (write_out) p.pre[r * 4 + g] = v;
+    } else {
+      const int i = g - 4;
+      const float v = 2.0f / (1.0f + expf(-(sm.hcs[1] * m[4 + i] + sm.hcb[4 + i])));
+      sm.post[r][i] = v;
+      if (write_out) p.post[r * 4 + i] = v;
+    }
+  }
+  /* Sinkhorn: 16 lanes per row hold M[i][j] at lane 16 (r % 4) + 4 i + j; row sums with quad
+   * butterflies, column sums with two rotations inside the 16-lane row (each lane associates
+   * its column sum in its own fixed order); each normalisation multiplies by the hardware
+   * reciprocal of the sum */
+  if (wave < (R + 3) / 4) {
+    const int r = wave * 4 + (lane >> 4), q = lane & 15;
+    const bool live = r < R;
+    const float* m = sm.mixes[live ? r : 0];
+    const float L = sm.hcs[2] * m[8 + q] + sm.hcb[8 + q];
+    float mx = fmaxf(L, dpp<0xB1>(L));
+    mx = fmaxf(mx, dpp<0x4E>(mx));
+    mx = fmaxf(mx, dpp<0x124>(mx)); /* row_ror:4 */
+    mx = fmaxf(mx, dpp<0x128>(mx)); /* row_ror:8 */
+    float M = expf(L - mx);
+    for (int it = 0; it < p.iters; ++it) {
+      float rs = M + dpp<0xB1>(M);
+      rs = rs + dpp<0x4E>(rs);
+      M = M * __builtin_amdgcn_rcpf(rs);
+      float cs = M + dpp<0x124>(M);
+      cs = cs + dpp<0x128>(cs);
+      M = M * __builtin_amdgcn_rcpf(cs);
+    }
+    if (live) {
+      sm.comb[r][q] = M;
+      if (write_out) p.comb[r * 16 + q] = M;
+    }
+  }
+  __syncthreads();
+  stamp(p, sm.trace_on != 0, 16);
+  /* collapse: x = bf16(sum_i pre_i state_i), VE consecutive positions per thread, 16-byte
+   * loads of the four streams; sum of squares of the rounded x */
+  float ss[RMAX];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) ss[r] = 0.0f;
+  constexpr int RB = RMAX < 4 ? RMAX : 4; /* rows whose loads are in flight together */
+  for (int c = tid; c < H / VE; c += kBlock) {
+#pragma unroll
+    for (int r0 = 0; r0 < RMAX; r0 += RB) {
+      if (r0 >= R) break;
+      uint4 sv[RB][4];
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        if (r0 + rr >= R) break;
+        const uint8_t* sbase = sm.state_in_lds
+                                   ? sm.big + ((size_t)R + 1) * H * ab
+                                   : static_cast<const uint8_t*>(p.state);
+        const uint8_t* base = sbase + ((size_t)(r0 + rr) * n + (size_t)c * VE) * ab;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sv[rr][i] = *reinterpret_cast<const uint4*>(base + (size_t)i * H * ab);
+      }
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        const int r = r0 + rr;
+        if (r >= R) break;
+        const float p0 = sm.pre[r][0], p1 = sm.pre[r][1], p2 = sm.pre[r][2], p3 = sm.pre[r][3];
+        const uint32_t a0[4] = {sv[rr][0].x, sv[rr][0].y, sv[rr][0].z, sv[rr][0].w};
+        const uint32_t a1[4] = {sv[rr][1].x, sv[rr][1].y, sv[rr][1].z, sv[rr][1].w};
+        const uint32_t a2[4] = {sv[rr][2].x, sv[rr][2].y, sv[rr][2].z, sv[rr][2].w};
+        const uint32_t a3[4] = {sv[rr][3].x, sv[rr][3].y, sv[rr][3].z, sv[rr][3].w};
+        uint32_t xo[4];
+        float xf[2];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          float v0, v1, v2, v3;
+          if (ACT == F32) {
+            v0 = __uint_as_float(a0[e]); v1 = __uint_as_float(a1[e]);
+            v2 = __uint_as_float(a2[e]); v3 = __uint_as_float(a3[e]);
+          } else {
+            const int sh = (e & 1) ? 16 : 0;
+            v0 = bf2f((a0[e >> 1] >> sh) & 0xFFFFu); v1 = bf2f((a1[e >> 1] >> sh) & 0xFFFFu);
+            v2 = bf2f((a2[e >> 1] >> sh) & 0xFFFFu); v3 = bf2f((a3[e >> 1] >> sh) & 0xFFFFu);
+          }
+          float a = p0 * v0;
+          a = fmaf(p1, v1, a);
+          a = fmaf(p2, v2, a);
+          a = fmaf(p3, v3, a);
+          if (ACT == F32) {
+            xo[e] = __float_as_uint(a);
+            ss[r] = fmaf(a, a, ss[r]);
+          } else {
+            xf[e & 1] = a;
+            if (e & 1) {
+              const uint32_t pr = f2bf2(xf[0], xf[1]);
+              xo[e >> 1] = pr;
+              const float x0 = bf2f(pr & 0xFFFFu), x1 = bf2f(pr >> 16);
+              ss[r] = fmaf(x0, x0, ss[r]);
+              ss[r] = fmaf(x1, x1, ss[r]);
+            }
+          }
+        }
+        const uint4 xv = make_uint4(xo[0], xo[1], xo[2], xo[3]);
+        const size_t byte = ((size_t)r * H + (size_t)c * VE) * ab;
+        *reinterpret_cast<uint4*>(sm.big + byte) = xv;
+        if (write_out && p.x) *reinterpret_cast<uint4*>(static_cast<uint8_t*>(p.x) + byte) = xv;
+      }
+    }
+  }
+  stamp(p, sm.trace_on != 0, 17);
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    if (r >= R) break;
+    const float t = wave_sum(ss[r]);
+    if (lane == 0) sm.red[wave][r] = t;
+  }
+  __syncthreads();
+  if (tid < R) {
+    float t = 0.0f;
+    for (int w = 0; w < kWaves; ++w) t += sm.red[w][tid];
+    sm.rsum[tid] = t;
+  }
+  __syncthreads();
+  stamp(p, sm.trace_on != 0, 18);
+  /* weighted RMSNorm: norm = bf16(x * (1 / sqrt(mean(x^2) + eps)) * w), VE positions per
+   * thread */
+  const uint8_t* wn = sm.big + (size_t)R * H * ab;
+  for (int r = 0; r < R; ++r) {
+    const float inv = 1.0f / sqrtf(sm.rsum[r] / (float)H + p.eps_norm);
+    for (int c = tid; c < H / VE; c += kBlock) {
+      const size_t byte = ((size_t)r * H + (size_t)c * VE) * ab;
+      const uint4 xv = *reinterpret_cast<const uint4*>(sm.big + byte);
+      const uint4 wv = *reinterpret_cast<const uint4*>(wn + (size_t)c * VE * ab);
+      const uint32_t xa[4] = {xv.x, xv.y, xv.z, xv.w}, wa[4] = {wv.x, wv.y, wv.z, wv.w};
+      uint32_t o[4];
+      float vf = 0.0f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        float xb, w;
+        if (ACT == F32) {
+          xb = __uint_as_float(xa[e]);
+          w = __uint_as_float(wa[e]);
+        } else {
+          const int sh = (e & 1) ? 16 : 0;
+          xb = bf2f((xa[e >> 1] >> sh) & 0xFFFFu);
+          w = bf2f((wa[e >> 1] >> sh) & 0xFFFFu);
+        }
+        const float v = xb * inv * w;
+        if (ACT == F32)
+          o[e] = __float_as_uint(v);
+        else if (e & 1)
+          o[e >> 1] = f2bf2(vf, v);
+        else
+          vf = v;
+      }
+      const uint4 ov = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(sm.big + byte) = ov;
+      if (write_out) *reinterpret_cast<uint4*>(static_cast<uint8_t*>(p.norm) + byte) = ov;
+    }
+  }
+  __syncthreads();
+}
+
+/* Copies R act rows [R][H] from global memory into sm.big. */
+template <int ACT>
+__device__ __forceinline__ void load_act_rows(const void* src, int R, int H, Smem& sm) {
+  const size_t bytes = (size_t)R * H * (ACT == F32 ? 4 : 2);
+  const uint4* s = static_cast<const uint4*>(src);
+  uint4* d = reinterpret_cast<uint4*>(sm.big);
+  for (size_t i = threadIdx.x; i < bytes / 16; i += kBlock) d[i] = s[i];
+  __syncthreads();
+}
+
+template <int ACT, int RMAX>
+__device__ __forceinline__ void act_rows_ptrs(const Params& p, const Smem& sm,
+                                              const void* (&arow)[RMAX]) {
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r)
+    arow[r] = sm.big + (size_t)(r < p.R ? r : 0) * p.H * (ACT == F32 ? 4 : 2);
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Phase: router logits [ds4 router commit: the F32 logits matvec]. One wave per expert row,
+ * rows spread over compute units first; the fused launch loads each wave's first row before
+ * the mix barrier. */
+typedef WRegs<F32, 1, 20> RouterRegs;
+
+/* Issues the loads of this wave's first router row chunk (task order of ph_router). */
+__device__ __forceinline__ void router_prefetch(const Params& p, RouterRegs& W) {
+  const int e = wave_major_id();
+  if (e < p.E) {
+    const uint8_t* vr[1] = {reinterpret_cast<const uint8_t*>(p.w_router + (size_t)e * p.H)};
+    const uint8_t* sr[1] = {nullptr};
+    wregs_load(W, vr, sr, p.H, 0);
+  }
+}
+
+template <int ACT, int RMAX, bool PRE>
+__device__ __forceinline__ void ph_router(const Params& p, const Smem& sm, const RouterRegs& pre) {
+  const int lane = threadIdx.x & 63;
+  const int nwt = gridDim.x * kWaves;
+  const void* arow[RMAX];
+  act_rows_ptrs<ACT, RMAX>(p, sm, arow);
+  const uint32_t mask = (1u << p.R) - 1u;
+  constexpr int EL = 4;
+  const int nsteps = (p.H + 64 * EL - 1) / (64 * EL);
+  for (int e = wave_major_id(); e < p.E; e += nwt) {
+    const uint8_t* vr[1] = {reinterpret_cast<const uint8_t*>(p.w_router + (size_t)e * p.H)};
+    const uint8_t* sr[1] = {nullptr};
+    float acc[RMAX];
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) acc[r] = 0.0f;
+    for (int s0 = 0; s0 < nsteps; s0 += 20) {
+      RouterRegs W;
+      if (PRE && s0 == 0 && e == wave_major_id())
+        W = pre;
+      else
+        wregs_load(W, vr, sr, p.H, s0);
+#pragma unroll
+      for (int c = 0; c < 20; ++c) {
+        const int k = ((s0 + c) * 64 + lane) * EL;
+        if (s0 + c < nsteps && k < p.H) {
+#pragma unroll
+          for (int r = 0; r < RMAX; ++r) {
+            if (!(mask & (1u << r))) continue;
+            float x0, x1, x2, x3;
+            if constexpr (ACT == F32) {
+              const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(arow[r]) + k);
+              x0 = x.x; x1 = x.y; x2 = x.z; x3 = x.w;
+            } else {
+              const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(arow[r]) + k);
+              x0 = bf2f(x.x & 0xFFFFu); x1 = bf2f(x.x >> 16);
+              x2 = bf2f(x.y & 0xFFFFu); x3 = bf2f(x.y >> 16);
+            }
+            float a = acc[r];
+            a = fmaf(__uint_as_float(W.v[0][c].x), x0, a);
+            a = fmaf(__uint_as_float(W.v[0][c].y), x1, a);
+            a = fmaf(__uint_as_float(W.v[0][c].z), x2, a);
+            a = fmaf(__uint_as_float(W.v[0][c].w), x3, a);
+            acc[r] = a;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      if (r >= p.R) break;
+      const float t = wave_sum(acc[r]);
+      if (lane == 0) stf_coh(p.logits + (size_t)r * p.E + e, t);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Phase: select, run by one whole workgroup for all rows [ds4 router commit: sqrt(softplus),
+ * the bias, the canonical (score descending, index ascending) top-k, normalised weights, the
+ * clamp, the row division and the scale as separately rounded ops; tie-order commit].
+ * One wave per row; lane L holds experts L, L + 64, ... as 64-bit keys (ordered biased score in
+ * the high word, complement of the index in the low word), so the largest key is the highest
+ * score and, among equal scores, the smallest index; k rounds of a DPP wave maximum pick the
+ * experts in canonical order. READING: the clamp floor is 2^-14; the bias steers selection
+ * only (the weights gather the unbiased scores). */
+__device__ __forceinline__ uint32_t ord_f32(float f) {
+  if (f != f) return 0u; /* NaN ranks last */
+  if (f == 0.0f) f = 0.0f;
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void key_max_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t oh = dpp_u<CTRL>(hi), ol = dpp_u<CTRL>(lo);
+  const bool take = oh > hi || (oh == hi && ol > lo);
+  hi = take ? oh : hi;
+  lo = take ? ol : lo;
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void key_max_bcast(uint32_t& hi, uint32_t& lo) {
+  /* lanes of rows outside ROWS keep their own value (old = src) */
+  const uint32_t oh = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROWS, 0xF, false);
+  const uint32_t ol = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROWS, 0xF, false);
+  const bool take = oh > hi || (oh == hi && ol > lo);
+  hi = take ? oh : hi;
+  lo = take ? ol : lo;
+}
+
+/* Largest 64-bit key (hi, lo) over the wave, returned (uniform) to every lane: butterflies
+ * inside each 16-lane row, then row broadcasts carry the maxima to the last row. */
+__device__ __forceinline__ uint64_t wave_max_key(uint32_t hi, uint32_t lo) {
+  key_max_step<0xB1>(hi, lo);
+  key_max_step<0x4E>(hi, lo);
+  key_max_step<0x141>(hi, lo);
+  key_max_step<0x140>(hi, lo);
+  key_max_bcast<0x142, 0xA>(hi, lo); /* row_bcast:15 into rows 1 and 3 */
+  key_max_bcast<0x143, 0xC>(hi, lo); /* row_bcast:31 into rows 2 and 3 */
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 63) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
+}
+
+template <int PER>
+__device__ __forceinline__ void select_row(const Params& p, Smem& sm, int r) {
+  const int lane = threadIdx.x & 63, E = p.E, K = p.K;
+  const __amdgpu_buffer_rsrc_t lg = coh_region(p.logits, (size_t)p.R * E * 4);
+  uint32_t khi[PER], klo[PER];
+  float sv[PER], zs[PER], bs[PER];
+#pragma unroll
+  for (int c = 0; c < PER; ++c) {
+    const int e = lane + 64 * c;
+    zs[c] = coh_f32(lg, (uint32_t)(((size_t)r * E + e) * 4));
+    bs[c] = e < E ? sm.bias[e] : 0.0f;
+  }
+#pragma unroll
+  for (int c = 0; c < PER; ++c) {
+    const int e = lane + 64 * c;
+    khi[c] = 0u;
+    klo[c] = 0u;
+    sv[c] = 0.0f;
+    if (e < E) {
+      const float z = zs[c];
+      const float sp = z > 0.0f ? z + log1pf(expf(-z)) : log1pf(expf(z));
+      const float sc = sqrtf(sp);
+      khi[c] = ord_f32(sc + bs[c]);
+      klo[c] = 0xFFFFFFFFu - (uint32_t)e;
+      sv[c] = sc;
+    }
+  }
+  stamp(p, sm.trace_on != 0, 19);
+  for (int j = 0; j < K; ++j) {
+    uint32_t bh = 0u, bl = 0u;
+#pragma unroll
+    for (int c = 0; c < PER; ++c) {
+      const bool take = khi[c] > bh || (khi[c] == bh && klo[c] > bl);
+      bh = take ? khi[c] : bh;
+      bl = take ? klo[c] : bl;
+    }
+    const uint64_t best = wave_max_key(bh, bl);
+    const uint32_t wh = (uint32_t)(best >> 32), wl = (uint32_t)best;
+#pragma unroll
+    for (int c = 0; c < PER; ++c) {
+      if (klo[c] == wl && khi[c] == wh && lane + 64 * c < E) {
+        sm.sel_e[r][j] = (int)(0xFFFFFFFFu - wl);
+        sm.sel_s[r][j] = sv[c];
+        khi[c] = 0u;
+        klo[c] = 0u;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void ph_select(const Params& p, Smem& sm, bool write_out) {
+  const int tid = threadIdx.x, wave = tid >> 6, K = p.K;
+  for (int r = wave; r < p.R; r += kWaves) {
+    if (p.E <= 256)
+      select_row<4>(p, sm, r);
+    else
+      select_row<kMaxExperts / 64>(p, sm, r); /* 8 candidates per lane */
+  }
+  __syncthreads();
+  if (tid < p.R) {
+    const int r = tid;
+    float sum = 0.0f;
+    for (int j = 0; j < K; ++j) sum += sm.sel_s[r][j];
+    const float c = fmaxf(sum, 6.103515625e-05f); /* 2^-14 */
+    for (int j = 0; j < K; ++j) {
+      const float w = (sm.sel_s[r][j] / c) * p.rho;
+      sm.sel_w[r][j] = w;
+      if (write_out) {
+        p.idx[r * K + j] = sm.sel_e[r][j];
+        p.weights[r * K + j] = w;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+/* Reads a caller-provided selection (idx, weights) into sm.sel_*; indices are clamped into
+ * [0, E) so a bad index cannot address outside the expert arrays. */
+__device__ __forceinline__ void load_selection(const Params& p, Smem& sm) {
+  const int tid = threadIdx.x;
+  if (tid < p.R * p.K) {
+    const int r = tid / p.K, j = tid % p.K;
+    int e = p.idx_in[tid];
+    e = e < 0 ? 0 : (e >= p.E ? p.E - 1 : e);
+    sm.sel_e[r][j] = e;
+    sm.sel_w[r][j] = p.w_in[tid];
+  }
+  __syncthreads();
+}
+
+/* Plan: the distinct selected experts in ascending order (each is streamed once for all the
+ * rows that chose it), with the rows that use it and the slot j it fills in each row. Item nU
+ * is the shared expert (every row). */
+__device__ __forceinline__ void ph_plan(const Params& p, Smem& sm) {
+  const int tid = threadIdx.x, R = p.R, K = p.K, E = p.E;
+  for (int e = tid; e < E; e += kBlock) sm.used[e] = 0;
+  __syncthreads();
+  if (tid < R * K) sm.used[sm.sel_e[tid / K][tid % K]] = 1;
+  __syncthreads();
+  if (tid < 64) {
+    int base = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + tid;
+      const bool u = e < E && sm.used[e];
+      const uint64_t bal = __ballot(u);
+      if (u) sm.U[base + __popcll(bal & ((1ull << tid) - 1ull))] = e;
+      base += __popcll(bal);
+    }
+    if (tid == 0) sm.nU = base;
+  }
+  __syncthreads();
+  const int nU = sm.nU;
+  for (int q = tid; q < (nU + 1) * kMaxRows; q += kBlock) {
+    const int u = q / kMaxRows, r = q % kMaxRows;
+    int slot = -1;
+    if (r < R) {
+      if (u == nU) {
+        slot = K;
+      } else {
+        for (int j = 0; j < K; ++j)
+          if (sm.sel_e[r][j] == sm.U[u]) slot = j;
+      }
+    }
+    sm.uslot[u][r] = (int8_t)slot;
+  }
+  __syncthreads();
+  if (tid <= nU) {
+    uint32_t m = 0;
+    for (int r = 0; r < R; ++r)
+      if (sm.uslot[tid][r] >= 0) m |= 1u << r;
+    sm.umask[tid] = m;
+  }
+  __syncthreads();
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Phase: gate/up + SwiGLU [ds4 router/shared commit: both matvecs, gate/up rounded to BF16
+ * before SwiGLU and the product after it]. Task (expert, intermediate row i): one wave streams
+ * gate row i and up row i once and applies them to every row that chose the expert.
+ * READING: routed experts use the shared expert's rounding points. */
+template <int ACT, int FMT, int RMAX>
+__device__ __forceinline__ void gateup_task(const Params& p, const Smem& sm, const Mat& m,
+                                            int e, int i, int inter, uint32_t mask, int u,
+                                            bool is_shared) {
+  const int H = p.H, lane = threadIdx.x & 63;
+  const size_t vb = row_vbytes(FMT, H), sb = row_sbytes(FMT, H);
+  const size_t row = (size_t)e * inter + i;
+  const uint8_t* vr[2] = {m.gate + row * vb, m.up + row * vb};
+  const uint8_t* sr[2] = {m.gate_s ? m.gate_s + row * sb : nullptr,
+                          m.up_s ? m.up_s + row * sb : nullptr};
+  const void* arow[RMAX];
+  act_rows_ptrs<ACT, RMAX>(p, sm, arow);
+  float acc[2][RMAX];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) acc[0][r] = acc[1][r] = 0.0f;
+  dot_rows<FMT, ACT, RMAX, 2, Fmt<FMT>::CH_GU>(vr, sr, H, arow, mask, acc);
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    if (!(mask & (1u << r))) continue;
+    const float g = act_round<ACT>(wave_sum(acc[0][r]));
+    const float uu = act_round<ACT>(wave_sum(acc[1][r]));
+    const float h = act_round<ACT>(g / (1.0f + expf(-g)) * uu);
+    if (lane == 0) {
+      if (is_shared)
+        act_st_coh<ACT>(p.h_shared, (size_t)r * p.Is + i, h);
+      else
+        act_st_coh<ACT>(p.h_routed, ((size_t)r * p.K + sm.uslot[u][r]) * p.I + i, h);
+    }
+  }
+}
+
+/* Shared-expert gate/up: Is tasks spread over compute units first. */
+template <int ACT, int SFMT, int RMAX>
+__device__ __forceinline__ void ph_gateup_shared(const Params& p, const Smem& sm) {
+  if (p.Is <= 0) return;
+  const int nwt = gridDim.x * kWaves;
+  const uint32_t mask = (1u << p.R) - 1u;
+  for (int i = wave_major_id(); i < p.Is; i += nwt)
+    gateup_task<ACT, SFMT, RMAX>(p, sm, p.shared, 0, i, p.Is, mask, 0, true);
+}
+
+/* Routed gate/up: the nU * I tasks split into equal contiguous ranges, one per wave. */
+template <int ACT, int RFMT, int RMAX>
+__device__ __forceinline__ void ph_gateup_routed(const Params& p, const Smem& sm) {
+  const long T = (long)sm.nU * p.I;
+  const long gw = (long)blockIdx.x * kWaves + (threadIdx.x >> 6), nwt = (long)gridDim.x * kWaves;
+  const long t0 = T * gw / nwt, t1 = T * (gw + 1) / nwt;
+  for (long t = t0; t < t1; ++t) {
+    const int u = (int)(t / p.I), i = (int)(t % p.I);
+    gateup_task<ACT, RFMT, RMAX>(p, sm, p.routed, sm.U[u], i, p.I, sm.umask[u], u, false);
+  }
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Phase: down projections, routed sum, shared rounding and block for the workgroup's slice of
+ * hidden rows [ds4 router/shared commit: the down projection rounded on its store, the routed +
+ * shared sum and its rounding]. The hidden rows of the selected experts are staged in LDS in
+ * groups; task (item, group of 4 consecutive output rows) is one wave. y values land in LDS;
+ * then per (h, r): routed = f32 sum_j w_j y_j (selection order), shared = bf16(y_s),
+ * block = bf16(routed + shared). Leaves block in sm for the expand. */
+struct DownGeo {
+  int h0, nh, hs;
+  float* y;   /* [hs][R][K + 1] */
+  float* blk; /* [hs][R] */
+};
+
+__device__ __forceinline__ DownGeo down_geo(const Params& p, Smem& sm) {
+  DownGeo g;
+  g.hs = (p.H + p.nslice - 1) / p.nslice;
+  g.h0 = blockIdx.x * g.hs;
+  g.nh = p.H - g.h0 < g.hs ? p.H - g.h0 : g.hs;
+  if (g.nh < 0) g.nh = 0;
+  g.y = reinterpret_cast<float*>(sm.big + kLdsHidBytes);
+  g.blk = g.y + (size_t)g.hs * p.R * (p.K + 1);
+  return g;
+}
+
+template <int ACT, int FMT>
+__device__ __forceinline__ void down_rows(const Params& p, const DownGeo& g, const Mat& m, int e,
+                                          int inter, int q, const uint8_t* (&vr)[kRG],
+                                          const uint8_t* (&sr)[kRG]) {
+  const size_t vb = row_vbytes(FMT, inter), sb = row_sbytes(FMT, inter);
+#pragma unroll
+  for (int c = 0; c < kRG; ++c) {
+    int hl = q * kRG + c;
+    if (hl >= g.nh) hl = g.nh - 1; /* duplicate a valid row; its result is discarded */
+    const size_t row = (size_t)e * p.H + g.h0 + hl;
+    vr[c] = m.down + row * vb;
+    sr[c] = m.down_s ? m.down_s + row * sb : nullptr;
+  }
+}
+
+template <int ACT, int FMT, int RMAX>
+__device__ __forceinline__ void down_task(const Params& p, const Smem& sm, const DownGeo& g,
+                                          const Mat& m, int e, int inter, int item, int q,
+                                          bool is_shared,
+                                          const WRegs<FMT, kRG, Fmt<FMT>::CH_DN>& pre,
+                                          bool use_pre) {
+  const int lane = threadIdx.x & 63;
+  constexpr int CH = Fmt<FMT>::CH_DN;
+  const uint8_t* vr[kRG];
+  const uint8_t* sr[kRG];
+  down_rows<ACT, FMT>(p, g, m, e, inter, q, vr, sr);
+  const uint32_t mask = sm.umask[item];
+  const void* arow[RMAX];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r)
+    arow[r] = sm.big + (size_t)((mask & (1u << r)) ? sm.voff[item][r] : 0) * 16;
+  float acc[kRG][RMAX];
+#pragma unroll
+  for (int c = 0; c < kRG; ++c)
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) acc[c][r] = 0.0f;
+  if (use_pre) {
+    wregs_dot<FMT, ACT, RMAX, kRG, CH>(pre, inter, 0, arow, mask, acc);
+    dot_rows<FMT, ACT, RMAX, kRG, CH>(vr, sr, inter, arow, mask, acc, CH);
+  } else {
+    dot_rows<FMT, ACT, RMAX, kRG, CH>(vr, sr, inter, arow, mask, acc);
+  }
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    if (!(mask & (1u << r))) continue;
+    const int slot = is_shared ? p.K : sm.uslot[item][r];
+#pragma unroll
+    for (int c = 0; c < kRG; ++c) {
+      const float t = wave_sum(acc[c][r]);
+      const int hl = q * kRG + c;
+      if (lane == 0 && hl < g.nh) g.y[((size_t)hl * p.R + r) * (p.K + 1) + slot] = t;
+    }
+  }
+}
+
+/* Items [first, last) whose hidden rows fit in the staging area (bytes and list entries). */
+__device__ __forceinline__ int down_group_end(const Params& p, const Smem& sm, int first,
+                                              size_t ab) {
+  const int nU = sm.nU;
+  int item = first, count = 0;
+  size_t used = 0;
+  while (item <= nU) {
+    const int inter = item == nU ? p.Is : p.I;
+    const int rows = __popc(sm.umask[item]);
+    const size_t need = (size_t)rows * inter * ab;
+    if (item > first && (used + need > (size_t)kLdsHidBytes || count + rows > kMaxStaged)) break;
+    used += need;
+    count += rows;
+    ++item;
+  }
+  return item;
+}
+
+/* In the fused launch (FUSED), the wait for the gate/up barrier runs after this wave has issued
+ * the loads of its first routed task (so they overlap the wait) and before any hidden row is
+ * read. */
+template <int ACT, int RFMT, int SFMT, int RMAX, bool FUSED>
+__device__ __forceinline__ bool ph_down(const Params& p, Smem& sm) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const DownGeo g = down_geo(p, sm);
+  const int nU = sm.nU, R = p.R;
+  const size_t ab = ACT == F32 ? 4 : 2;
+  const int nq = (g.nh + kRG - 1) / kRG;
+  constexpr int CHR = Fmt<RFMT>::CH_DN;
+  /* prefetch: first task of this wave in the first group, if routed */
+  int last = down_group_end(p, sm, 0, ab);
+  WRegs<RFMT, kRG, CHR> pre;
+  WRegs<SFMT, kRG, Fmt<SFMT>::CH_DN> none;
+  bool have_pre = false;
+  if (RMAX == 1 && wave < last * nq && wave / nq < nU) {
+    const uint8_t* vr[kRG];
+    const uint8_t* sr[kRG];
+    down_rows<ACT, RFMT>(p, g, p.routed, sm.U[wave / nq], p.I, wave % nq, vr, sr);
+    wregs_load(pre, vr, sr, p.I, 0);
+    have_pre = true;
+  }
+  if (FUSED) {
+    if (!bar_wait(p, sm, PH_GATEUP)) return false;
+    stamp(p, sm.trace_on != 0, 10);
+  }
+  int first = 0;
+  while (first <= nU) {
+    if (first > 0) last = down_group_end(p, sm, first, ab);
+    __syncthreads(); /* the previous group's tasks are done with the staging area */
+    if (tid == 0) {
+      size_t off = 0;
+      for (int it = first; it < last; ++it) {
+        const int inter = it == nU ? p.Is : p.I;
+        for (int r = 0; r < R; ++r)
+          if (sm.umask[it] & (1u << r)) {
+            sm.voff[it][r] = (uint16_t)(off / 16);
+            off += (size_t)inter * ab;
+          }
+      }
+    }
+    __syncthreads();
+    /* list the group's hidden rows, then copy them with batched coherent 16-byte loads */
+    if (tid == 0) {
+      int nv = 0;
+      for (int it = first; it < last; ++it)
+        for (int r = 0; r < R; ++r)
+          if (sm.umask[it] & (1u << r)) {
+            const size_t vbytes = (size_t)(it == nU ? p.Is : p.I) * ab;
+            sm.vsrc[nv] = it == nU ? (uint32_t)(kHidShared | (r * vbytes))
+                                   : (uint32_t)(((size_t)r * p.K + sm.uslot[it][r]) * vbytes);
+            sm.vdst[nv] = sm.voff[it][r];
+            sm.vlen[nv] = (uint16_t)(vbytes / 16);
+            ++nv;
+          }
+      sm.nv = nv;
+    }
+    __syncthreads();
+    {
+      const __amdgpu_buffer_rsrc_t hr =
+          coh_region(p.h_routed, (size_t)R * p.K * p.I * ab);
+      const __amdgpu_buffer_rsrc_t hsr =
+          coh_region(p.h_shared, (size_t)R * (p.Is > 0 ? p.Is : 1) * ab);
+      const int nv = sm.nv;
+      constexpr int B = 4;
+      for (int v0 = 0; v0 < nv; v0 += B) {
+        uint4 buf[B][2];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int v = v0 + b, ch = tid + h * kBlock;
+            buf[b][h] = make_uint4(0, 0, 0, 0);
+            if (v < nv && ch < sm.vlen[v]) {
+              const uint32_t src = sm.vsrc[v];
+              buf[b][h] = (src & kHidShared) ? coh_b128(hsr, (src & ~kHidShared) + ch * 16)
+                                             : coh_b128(hr, src + ch * 16);
+            }
+          }
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int v = v0 + b, ch = tid + h * kBlock;
+            if (v < nv && ch < sm.vlen[v])
+              *reinterpret_cast<uint4*>(sm.big + (size_t)sm.vdst[v] * 16 + (size_t)ch * 16) = buf[b][h];
+          }
+      }
+    }
+    __syncthreads();
+    if (FUSED && first == 0) stamp(p, sm.trace_on != 0, 21);
+    const int ntask = (last - first) * nq;
+    for (int t = wave; t < ntask; t += kWaves) {
+      const int it = first + t / nq, q = t % nq;
+      if (it == nU) {
+        if (p.Is > 0 && sm.umask[it])
+          down_task<ACT, SFMT, RMAX>(p, sm, g, p.shared, 0, p.Is, it, q, true, none, false);
+      } else {
+        const bool use_pre = have_pre && first == 0 && t == wave;
+        down_task<ACT, RFMT, RMAX>(p, sm, g, p.routed, sm.U[it], p.I, it, q, false, pre, use_pre);
+      }
+    }
+    first = last;
+  }
+  __syncthreads();
+  /* combine */
+  for (int q = tid; q < g.nh * R; q += kBlock) {
+    const int hl = q / R, r = q % R;
+    const float* y = g.y + ((size_t)hl * R + r) * (p.K + 1);
+    float routed = 0.0f;
+    for (int j = 0; j < p.K; ++j) routed = fmaf(sm.sel_w[r][j], y[j], routed);
+    const float shared = p.Is > 0 ? act_round<ACT>(y[p.K]) : 0.0f;
+    const float blk = act_round<ACT>(routed + shared);
+    const size_t o = (size_t)r * p.H + g.h0 + hl;
+    if (p.routed_out) p.routed_out[o] = routed;
+    if (p.shared_out) act_st<ACT>(p.shared_out, o, shared);
+    if (p.block) act_st<ACT>(p.block, o, blk);
+    g.blk[q] = blk;
+  }
+  __syncthreads();
+  return true;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Phase: expand + carry for the workgroup's slice [ds4 HC fusion commit: post/comb expand +
+ * BF16; SGLang fused post/pre page: bf16 residual materialisation + next pre-norm GEMM
+ * partials + RMS square-sum partials]. new[i][h] = bf16(post_i block[h] + sum_j comb[i][j]
+ * state_j[h]). The carry is taken on the rounded new state; per-workgroup partials are summed
+ * in workgroup order by the last workgroup to finish. */
+template <int ACT, int RMAX, bool FUSED>
+__device__ __forceinline__ void ph_expand(const Params& p, Smem& sm, const float* blk) {
+  const int tid = threadIdx.x;
+  const int hs = (p.H + p.nslice - 1) / p.nslice;
+  const int h0 = blockIdx.x * hs;
+  int nh = p.H - h0 < hs ? p.H - h0 : hs;
+  if (nh < 0) nh = 0;
+  const int R = p.R, H = p.H, n = 4 * H;
+  /* new state: one thread per hidden position reads all 4 streams and writes all 4, so the
+   * output may alias the input */
+  float* nvb = reinterpret_cast<float*>(sm.big); /* [nh][R][4] */
+  for (int hl = tid; hl < nh; hl += kBlock) {
+    const int h = h0 + hl;
+    for (int r = 0; r < R; ++r) {
+      const size_t sb = (size_t)r * n + h;
+      const float s0 = act_ld<ACT>(p.state, sb), s1 = act_ld<ACT>(p.state, sb + H);
+      const float s2 = act_ld<ACT>(p.state, sb + 2 * (size_t)H);
+      const float s3 = act_ld<ACT>(p.state, sb + 3 * (size_t)H);
+      const float b = blk[hl * R + r];
+      float nv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float a = sm.post[r][i] * b;
+        a = fmaf(sm.comb[r][4 * i + 0], s0, a);
+        a = fmaf(sm.comb[r][4 * i + 1], s1, a);
+        a = fmaf(sm.comb[r][4 * i + 2], s2, a);
+        a = fmaf(sm.comb[r][4 * i + 3], s3, a);
+        nv[i] = act_round<ACT>(a);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        act_st<ACT>(p.state_out, sb + (size_t)i * H, nv[i]);
+        nvb[(hl * R + r) * 4 + i] = nv[i];
+      }
+    }
+  }
+  if (p.w_mix_next == nullptr) {
+    if (FUSED) arrive_last(p, sm); /* keeps every end counter advancing once per launch */
+    return;
+  }
+  stamp(p, sm.trace_on != 0, 12);
+  __syncthreads();
+  /* carry partials of this slice: cp[j][r][hl] = sum_i W_next[j][i H + h] new[r][i] (j < 24),
+   * cp[24][r][hl] = sum_i new[r][i]^2; then summed over hl in order */
+  float* cp = nvb + (size_t)nh * R * 4; /* [25][R][nh] */
+  for (int q = tid; q < nh * kNCarry; q += kBlock) {
+    const int hl = q % nh, j = q / nh, h = h0 + hl;
+    float w[4];
+    if (j < kNMix) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = p.w_mix_next[(size_t)j * n + (size_t)i * H + h];
+    }
+    for (int r = 0; r < R; ++r) {
+      const float* v = nvb + (hl * R + r) * 4;
+      float a;
+      if (j < kNMix) {
+        a = w[0] * v[0];
+        a = fmaf(w[1], v[1], a);
+        a = fmaf(w[2], v[2], a);
+        a = fmaf(w[3], v[3], a);
+      } else {
+        a = v[0] * v[0];
+        a = fmaf(v[1], v[1], a);
+        a = fmaf(v[2], v[2], a);
+        a = fmaf(v[3], v[3], a);
+      }
+      cp[((size_t)j * R + r) * nh + hl] = a;
+    }
+  }
+  __syncthreads();
+  if (tid < R * kNCarry) {
+    const int j = tid % kNCarry, r = tid / kNCarry;
+    const float* c = cp + ((size_t)j * R + r) * nh;
+    float t = 0.0f;
+    for (int hl = 0; hl < nh; ++hl) t += c[hl];
+    stf_coh(p.carry_part + (size_t)blockIdx.x * R * kNCarry + tid, t);
+  }
+  /* the last workgroup to finish sums the partials in workgroup order */
+  if (FUSED ? arrive_last(p, sm) : arrive_last_single(p, sm)) {
+    /* every wave takes (row, output) pairs; lanes take workgroups w = lane + 64 m */
+    const int lane = tid & 63, wave = tid >> 6;
+    const __amdgpu_buffer_rsrc_t cpr = coh_region(p.carry_part, (size_t)gridDim.x * R * kNCarry * 4);
+    for (int q = wave; q < R * kNCarry; q += kWaves) {
+      float t = 0.0f;
+      for (int w = lane; w < (int)gridDim.x; w += 64)
+        t += coh_f32(cpr, (uint32_t)(((size_t)w * R * kNCarry + q) * 4));
+      t = wave_sum(t);
+      if (lane == 0) {
+        p.carry_out[q] = t;
+        if (p.carry_ws) p.carry_ws[q] = t;
+      }
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Kernels */
+
+template <int ACT, int RMAX>
+__global__ void __launch_bounds__(kBlock) k_mix_partials(Params p) {
+  ph_mix_partials<ACT, RMAX>(p);
+}
+
+template <int ACT, int RMAX>
+__global__ void __launch_bounds__(kBlock) k_hc_pre(Params p) {
+  __shared__ Smem sm;
+  if (threadIdx.x == 0) sm.trace_on = 0;
+  load_pre_params<ACT>(p, sm);
+  __syncthreads();
+  ph_hc_pre<ACT, RMAX>(p, sm, true);
+}
+
+template <int ACT, int RMAX>
+__global__ void __launch_bounds__(kBlock) k_router_logits(Params p) {
+  __shared__ Smem sm;
+  load_act_rows<ACT>(p.norm_in, p.R, p.H, sm);
+  RouterRegs none;
+  ph_router<ACT, RMAX, false>(p, sm, none);
+}
+
+template <int UNUSED>
+__global__ void __launch_bounds__(kBlock) k_select(Params p) {
+  __shared__ Smem sm;
+  if (threadIdx.x == 0) sm.trace_on = 0;
+  load_bias(p, sm);
+  __syncthreads();
+  ph_select(p, sm, true);
+}
+
+template <int ACT, int RFMT, int SFMT, int RMAX>
+__global__ void __launch_bounds__(kBlock) k_gateup(Params p) {
+  __shared__ Smem sm;
+  load_act_rows<ACT>(p.norm_in, p.R, p.H, sm);
+  load_selection(p, sm);
+  ph_plan(p, sm);
+  ph_gateup_shared<ACT, SFMT, RMAX>(p, sm);
+  ph_gateup_routed<ACT, RFMT, RMAX>(p, sm);
+}
+
+template <int ACT, int RFMT, int SFMT, int RMAX>
+__global__ void __launch_bounds__(kBlock) k_down(Params p) {
+  __shared__ Smem sm;
+  if (threadIdx.x == 0) sm.trace_on = 0;
+  load_selection(p, sm);
+  ph_plan(p, sm);
+  ph_down<ACT, RFMT, SFMT, RMAX, false>(p, sm);
+}
+
+template <int ACT, int RMAX>
+__global__ void __launch_bounds__(kBlock) k_expand(Params p) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x;
+  if (tid < p.R * 4) sm.post[tid / 4][tid % 4] = p.post_in[tid];
+  if (tid < p.R * 16) sm.comb[tid / 16][tid % 16] = p.comb_in[tid];
+  const int hs = (p.H + p.nslice - 1) / p.nslice, h0 = blockIdx.x * hs;
+  int nh = p.H - h0 < hs ? p.H - h0 : hs;
+  if (nh < 0) nh = 0;
+  float* blk = reinterpret_cast<float*>(sm.big + kLdsHidBytes);
+  for (int q = tid; q < nh * p.R; q += kBlock) {
+    const int hl = q / p.R, r = q % p.R;
+    blk[q] = act_ld<ACT>(p.block_in, (size_t)r * p.H + h0 + hl);
+  }
+  __syncthreads();
+  ph_expand<ACT, RMAX, false>(p, sm, blk);
+}
+
+/* The whole layer half in one persistent launch (one workgroup per compute unit):
+ *   mix partials | arrive 1, load the pre-side parameters, wait 1 | pre side (every workgroup)
+ *   | router rows | arrive 2, shared-expert gate/up, wait 2 | select + plan (every workgroup)
+ *   | routed gate/up | arrive 3, issue the first down-projection loads, wait 3 | down, block
+ *   | expand + carry (the last workgroup to finish sums the carry).
+ * Trace slots: 0 start, 1 mix partials, 2 pre-side inputs ready, 3 pre side, 4 router,
+ * 5 shared gate/up, 6 router barrier passed, 7 select, 8 plan, 9 routed gate/up,
+ * 10 gate/up barrier passed, 11 down + block, 12 expand, 13 carry. */
+template <int ACT, int RFMT, int SFMT, int RMAX>
+__global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
+  __shared__ Smem sm;
+  bar_setup(p, sm);
+  __syncthreads();
+  const bool tr = sm.trace_on != 0;
+  stamp(p, tr, 0);
+  RouterRegs rpre;
+  if (!p.carry_in) {
+    ph_mix_partials<ACT, RMAX>(p);
+    stamp(p, tr, 1);
+    bar_arrive(p, sm, PH_MIX);
+  } else {
+    bar_arrive(p, sm, PH_MIX); /* keeps every barrier counter advancing once per launch */
+  }
+  router_prefetch(p, rpre);
+  load_pre_params<ACT>(p, sm);
+  load_bias(p, sm);
+  if (!p.carry_in) {
+    if (!bar_wait(p, sm, PH_MIX)) return;
+  } else {
+    __syncthreads();
+  }
+  stamp(p, tr, 2);
+  ph_hc_pre<ACT, RMAX>(p, sm, blockIdx.x == 0);
+  stamp(p, tr, 3);
+  ph_router<ACT, RMAX, true>(p, sm, rpre);
+  stamp(p, tr, 4);
+  bar_arrive(p, sm, PH_ROUTER);
+  ph_gateup_shared<ACT, SFMT, RMAX>(p, sm);
+  stamp(p, tr, 5);
+  if (!bar_wait(p, sm, PH_ROUTER)) return;
+  stamp(p, tr, 6);
+  ph_select(p, sm, blockIdx.x == 0);
+  stamp(p, tr, 7);
+  ph_plan(p, sm);
+  stamp(p, tr, 8);
+  ph_gateup_routed<ACT, RFMT, RMAX>(p, sm);
+  stamp(p, tr, 9);
+  bar_arrive(p, sm, PH_GATEUP);
+  if (!ph_down<ACT, RFMT, SFMT, RMAX, true>(p, sm)) return;
+  stamp(p, tr, 11);
+  const DownGeo g = down_geo(p, sm);
+  ph_expand<ACT, RMAX, true>(p, sm, g.blk);
+  stamp(p, tr, 13);
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Launch templates */
+
+#define MONO_LAUNCH(KERNEL, GRID)                                                      \
+  do {                                                                                 \
+    hipLaunchKernelGGL((KERNEL), dim3(GRID), dim3(kBlock), 0, st, p);                  \
+    return (int)hipGetLastError();                                                     \
+  } while (0)
+
+template <int ACT, int RFMT, int SFMT, int RMAX>
+int launch_fmt(Kernel k, const Params& p, int grid, hipStream_t st) {
+  switch (k) {
+    case K_GATEUP: MONO_LAUNCH((k_gateup<ACT, RFMT, SFMT, RMAX>), grid);
+    case K_DOWN: MONO_LAUNCH((k_down<ACT, RFMT, SFMT, RMAX>), grid);
+    case K_FFN_LAYER: MONO_LAUNCH((k_ffn_layer<ACT, RFMT, SFMT, RMAX>), grid);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mono
+
+#endif /* MONOLAYER_KERNELS_H */

@@ -151,6 +151,8 @@ class Gpu:
             self.buf(R * 25 * 4) if w_next is not None else None)
         mono.mono_ffn_layer(s, L, w_next, state, carry_in, new, carry, self.ws, stream())
         torch.cuda.synchronize()
+        st, err = mono.mono_workspace_poll(self.ws, stream())
+        assert st == mono.MONO_OK, "device-side wait expired: %s" % err
         adt, ws = self.adt, self.ws
         T = lambda which, dt, dims: ws_tensor(s, ws, which, dt, dims)
         out = dict(
