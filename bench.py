@@ -133,18 +133,22 @@ def summarize(res, cfg):
         achieved_gbs_median=float(np.median(gbs)))
 
 
-def cpu_baseline(cfg, budget_s: float):
-    """The oracle, timed on the host cores over whole layer-half steps of the same workload
-    (selected experts generated on the host outside the timed region)."""
+def cpu_baseline(cfg, budget_s: float, n_inputs: int = 4):
+    """The oracle, timed on the host cores over whole layer-half steps of the same workload.
+
+    Steps cycle over `n_inputs` seeded input states; the selected experts' weights are
+    generated on the host outside the timed region and kept for later steps."""
     import oracle
     import synth
     s = oracle.shape_of(cfg)
     d0, d1 = synth.dense_host(cfg, 0), synth.dense_host(cfg, 1)
     shared = synth.expert_host(cfg, 0, None)
+    states = [synth.state_host(cfg, i) for i in range(n_inputs)]
+    cache = {}
     done, spent = 0, 0.0
-    while spent < budget_s and done < 64:
-        st = synth.state_host(cfg, done)
-        # routing first (timed), then experts generated (untimed), then the rest (timed)
+    while spent < budget_s:
+        st = states[done % n_inputs]
+        # routing (timed), then any missing expert weights generated (untimed), then the rest
         t0 = time.perf_counter()
         mixes = oracle.mix(s, st, d0["w_mix"])
         pre, post, comb = oracle.split(s, mixes, d0["hc_scale"], d0["hc_base"])
@@ -152,16 +156,78 @@ def cpu_baseline(cfg, budget_s: float):
         lg = oracle.router_logits(s, norm, d0["w_router"])
         idx, w, _ = oracle.select(s, lg, d0["bias"])
         spent += time.perf_counter() - t0
-        ex = {int(e): synth.expert_host(cfg, 0, int(e)) for e in np.unique(idx)}
+        for e in np.unique(idx):
+            if int(e) not in cache:
+                cache[int(e)] = synth.expert_host(cfg, 0, int(e))
+        ex = {int(e): cache[int(e)] for e in np.unique(idx)}
         t0 = time.perf_counter()
         m = oracle.moe(s, norm, idx, w, cfg.routed_fmt, ex, cfg.shared_fmt, shared)
         oracle.expand(s, st, m["block"], post, comb, d1["w_mix"])
         spent += time.perf_counter() - t0
         done += 1
     return dict(value=done / spent, unit="steps/s", cores=oracle.threads(), kind="oracle",
-                sample="%d full layer-half steps of the same workload (%s), %.1f s of oracle "
-                       "compute; expert weights generated outside the timed region"
-                       % (done, cfg.name, spent))
+                sample="%d full layer-half steps of the same workload (%s) cycling over %d "
+                       "seeded inputs, %.1f s of oracle compute; expert weights generated "
+                       "outside the timed region" % (done, cfg.name, n_inputs, spent))
+
+
+# ---- HBM traffic from rocprofv3 counters -------------------------------------------------
+
+KERNEL_SOURCES = ["mono_kernels.h", "mono_internal.h", "mono_launch.hip", "mono_k_bf16.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_ffn_layer_bf16_r1_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "moe_decode_layer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the 1-row kernel recorded from FETCH_SIZE/WRITE_SIZE runs, or
+    None when the file is absent or the kernel sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                vals[k.strip("` ")] = v.strip().strip("`")
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _counter_rows(path):
+    import csv
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def pmc_summary(fetch_csv: str, write_csv: str):
+    """Per-kernel mean FETCH_SIZE and WRITE_SIZE (KiB per dispatch) and dispatch counts from
+    two rocprofv3 --pmc counter CSVs."""
+    agg = {}
+    for path, ctr in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        for r in _counter_rows(path):
+            if r.get("Counter_Name") != ctr:
+                continue
+            name = r["Kernel_Name"]
+            key = (name, ctr)
+            d = agg.setdefault(key, {})
+            # one value per dispatch (summed over dimensions if split)
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, ctr), d in agg.items():
+        out.setdefault(name, {})[ctr] = (float(np.mean(list(d.values()))), len(d))
+    return out
 
 
 def main():
@@ -173,7 +239,16 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-rows6", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="first run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc counter CSVs and exit (no GPU use)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        for name, d in sorted(pmc_summary(*args.pmc_summary).items()):
+            print("%s\t%s" % (name, "\t".join("%s=%.1f KiB x%d" % (c, v, n)
+                                              for c, (v, n) in sorted(d.items()))))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d "
               "refused)" % args.gpus, file=sys.stderr)
@@ -184,6 +259,16 @@ def main():
     import synth
     mono.lib()  # fails loudly when the HIP library is not built
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 2.0, out=dst)   # reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        log("  copy calibration: 5 x elementwise copy of %d MiB" % args.copy_calib_mib)
+        del src, dst
 
     cfg1 = synth.CONFIGS[2]
     log("building workloads")
@@ -226,7 +311,9 @@ def main():
                    "launch": "mono_ffn_layer, one persistent launch per step"},
         "roofline": {"bound": "hbm", "achieved": r1["achieved_gbs"], "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": r1["achieved_gbs"] / PEAK_HBM_GBS,
-                     "traffic": None},
+                     "traffic": recorded_traffic(),
+                     "algorithmic_bytes": r1["bytes_per_step_mean"],
+                     "kernel_source_hash": kernel_source_hash()},
         "launch_us": {"median": r1["launch_us_median"], "p10": r1["launch_us_p10"],
                       "p90": r1["launch_us_p90"], "mean": r1["launch_us_mean"]},
         "bytes_per_step": r1["bytes_per_step_mean"],

@@ -65,9 +65,15 @@ typedef enum {
   MONO_E_TIMEOUT = -4      /* a device-side bounded wait expired (mono_workspace_poll) */
 } mono_status;
 
-/* Shape of one layer-half step. Limits: 0 <= rows <= 8; n_streams == 4; hidden, inter and
- * shared_inter multiples of 256 (128 is accepted for inter and shared_inter when the expert
- * format is f32 or bf16); 1 <= top_k <= 16, top_k <= n_experts <= 512; act f32 or bf16. */
+/* Shape of one layer-half step. Limits (checked on the host, every failure listed):
+ *   0 <= rows <= 8; n_streams == 4; hidden a positive multiple of 64; inter a positive multiple
+ *   of 32 and shared_inter a non-negative multiple of 32; 1 <= top_k <= 16 and
+ *   top_k <= n_experts <= 512; act MONO_F32 or MONO_BF16; 0 <= sinkhorn_iters <= 1000;
+ *   routed_scale finite; eps_hc, eps_norm >= 0.
+ *   On-chip buffers (ab = 4 for f32, 2 for bf16 activations): (rows + 1) * hidden * ab <=
+ *   114688 bytes, rows * max(inter, shared_inter) * ab <= 81920 bytes and
+ *   max(inter, shared_inter) * ab <= 16384 bytes, and the slice of hidden positions one
+ *   workgroup expands must fit its LDS on the current device (MONO_E_UNSUPPORTED otherwise). */
 typedef struct {
   int rows;         /* R: decode rows (tokens) in the step */
   int hidden;       /* H */

@@ -80,9 +80,6 @@ void check_shape(Check& c, const mono_shape* s) {
   if (!(s->eps_hc >= 0.0f) || !(s->eps_norm >= 0.0f)) c.fail(MONO_E_INVAL, "eps_hc / eps_norm must be >= 0");
   if (act_ok(s->act) && s->rows > 0 && s->hidden > 0) {
     const size_t ab = s->act == MONO_F32 ? 4 : 2;
-    if ((size_t)s->rows * s->hidden * ab > (size_t)kLdsActBytes)
-      c.fail(MONO_E_UNSUPPORTED, "rows*hidden*%zu = %zu bytes exceeds the %d-byte activation buffer",
-             ab, (size_t)s->rows * s->hidden * ab, kLdsActBytes);
     const size_t wide = (size_t)(s->inter > s->shared_inter ? s->inter : s->shared_inter);
     if ((size_t)s->rows * wide * ab > (size_t)kLdsHidBytes)
       c.fail(MONO_E_UNSUPPORTED, "rows*max(inter, shared_inter)*%zu exceeds the %d-byte hidden-row buffer",
@@ -331,7 +328,6 @@ mono_status mono_hc_mix_collapse(const mono_shape* shape, const void* state,
   Check c;
   check_shape(c, shape);
   c.req(layer != nullptr, "layer is NULL");
-  c.ptr(ws, "ws", 256);
   if (c.code == MONO_OK) {
     c.ptr(state, "state", 16);
     if (!carry_in) c.ptr(layer->w_mix, "layer.w_mix", 16);
@@ -343,6 +339,7 @@ mono_status mono_hc_mix_collapse(const mono_shape* shape, const void* state,
     if (mixes) c.ptr(mixes, "mixes");
     if (x) c.ptr(x, "x", 16);
   }
+  c.ptr(ws, "ws", 256);
   if (c.code != MONO_OK || shape->rows == 0) return c.done();
   const int grid = device_grid(c, shape);
   if (c.code != MONO_OK) return c.done();
@@ -362,7 +359,6 @@ mono_status mono_router_select(const mono_shape* shape, const void* norm,
   Check c;
   check_shape(c, shape);
   c.req(layer != nullptr, "layer is NULL");
-  c.ptr(ws, "ws", 256);
   if (c.code == MONO_OK) {
     c.ptr(norm, "norm", 16);
     c.ptr(layer->w_router, "layer.w_router", 16);
@@ -370,6 +366,7 @@ mono_status mono_router_select(const mono_shape* shape, const void* norm,
     c.ptr(idx, "idx"); c.ptr(weights, "weights");
     if (logits) c.ptr(logits, "logits");
   }
+  c.ptr(ws, "ws", 256);
   if (c.code != MONO_OK || shape->rows == 0) return c.done();
   const int grid = device_grid(c, shape);
   if (c.code != MONO_OK) return c.done();
@@ -390,7 +387,6 @@ mono_status mono_moe_experts(const mono_shape* shape, const void* norm, const in
   Check c;
   check_shape(c, shape);
   c.req(layer != nullptr, "layer is NULL");
-  c.ptr(ws, "ws", 256);
   if (c.code == MONO_OK) {
     check_formats(c, shape, layer, true, true);
     c.ptr(norm, "norm", 16); c.ptr(idx, "idx"); c.ptr(weights, "weights"); c.ptr(block, "block", 4);
@@ -399,6 +395,7 @@ mono_status mono_moe_experts(const mono_shape* shape, const void* norm, const in
     if (shared_out) c.ptr(shared_out, "shared_out", 4);
     if (routed_out) c.ptr(routed_out, "routed_out");
   }
+  c.ptr(ws, "ws", 256);
   if (c.code != MONO_OK || shape->rows == 0) return c.done();
   const int grid = device_grid(c, shape);
   if (c.code != MONO_OK) return c.done();
@@ -421,7 +418,6 @@ mono_status mono_hc_expand(const mono_shape* shape, const void* state, const voi
                            void* new_state, float* carry_out, void* ws, void* stream) {
   Check c;
   check_shape(c, shape);
-  c.ptr(ws, "ws", 256);
   if (c.code == MONO_OK) {
     c.ptr(state, "state", 16); c.ptr(block, "block", 4); c.ptr(post, "post"); c.ptr(comb, "comb");
     c.ptr(new_state, "new_state", 16);
@@ -431,6 +427,7 @@ mono_status mono_hc_expand(const mono_shape* shape, const void* state, const voi
     }
     if (state && new_state && state == new_state) c.fail(MONO_E_INVAL, "new_state aliases state");
   }
+  c.ptr(ws, "ws", 256);
   if (c.code != MONO_OK || shape->rows == 0) return c.done();
   const int grid = device_grid(c, shape);
   if (c.code != MONO_OK) return c.done();
@@ -450,7 +447,6 @@ mono_status mono_ffn_layer(const mono_shape* shape, const mono_layer* layer,
   Check c;
   check_shape(c, shape);
   c.req(layer != nullptr, "layer is NULL");
-  c.ptr(ws, "ws", 256);
   if (c.code == MONO_OK) {
     check_formats(c, shape, layer, true, true);
     c.ptr(state_in, "state_in", 16);
@@ -469,6 +465,7 @@ mono_status mono_ffn_layer(const mono_shape* shape, const mono_layer* layer,
       c.ptr(carry_out, "carry_out");
     }
   }
+  c.ptr(ws, "ws", 256);
   if (c.code != MONO_OK || shape->rows == 0) return c.done();
   const int grid = device_grid(c, shape);
   if (c.code != MONO_OK) return c.done();

@@ -1,5 +1,5 @@
 /*
- * libmonolayer internals shared by the device code (mono_device.hip) and the
+ * libmonolayer internals shared by the device code (mono_kernels.h) and the
  * host code (mono_api.cpp): kernel parameter block, workspace layout, limits.
  */
 #ifndef MONOLAYER_INTERNAL_H
@@ -110,6 +110,9 @@ struct WsLayout {
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+/* Phase timestamps per workgroup in the trace region. */
+constexpr int kTraceSlots = 32;
+
 inline WsLayout ws_layout(const mono_shape& s) {
   const size_t R = s.rows > 0 ? s.rows : 1, H = s.hidden, E = s.n_experts, k = s.top_k,
                I = s.inter, Is = s.shared_inter;
@@ -140,12 +143,12 @@ inline WsLayout ws_layout(const mono_shape& s) {
   L.routed = take(R * H * 4);
   L.block = take(R * H * ab);
   L.carry = take(R * kNCarry * 4);
-  L.trace = take((size_t)kMaxGrid * 16 * 8);
+  L.trace = take((size_t)kMaxGrid * kTraceSlots * 8);
   L.total = o;
   return L;
 }
 
-/* Launchers (mono_device.hip). Each returns a hipError_t as int. */
+/* Launchers (mono_launch.hip). Each returns a hipError_t as int. */
 enum Kernel {
   K_MIX_PARTIALS,
   K_HC_PRE,
@@ -158,7 +161,6 @@ enum Kernel {
   K_WS_INIT,
   K_WS_DEBUG
 };
-constexpr int kTraceSlots = 32;
 int launch(Kernel k, const Params& p, int act, int rfmt, int sfmt, int grid, void* stream);
 int grid_size_for_device(int device);
 int max_active_persistent(int act, int rfmt, int sfmt, int rows);

@@ -208,6 +208,32 @@ def test_expand_identity_comb_zero_post_returns_state():
     np.testing.assert_array_equal(new, st)
 
 
+def test_expand_permutation_comb_moves_streams():
+    # comb as a permutation matrix (comb[i][perm[i]] = 1): new_i = state_perm[i] (the reading
+    # new_i = sum_j comb_ij * state_j); the 4-cycle is not symmetric, so comb^T would fail
+    s = small_shape(rows=2, act="bf16")
+    st = to_bf(np.random.default_rng(13).standard_normal((2, 4, 64)))
+    block = to_bf(np.random.default_rng(14).standard_normal((2, 64)))
+    perm = [1, 2, 3, 0]
+    comb = np.zeros((2, 4, 4), np.float32)
+    for i, j in enumerate(perm):
+        comb[:, i, j] = 1.0
+    new, _ = oracle.expand(s, st, block, np.zeros((2, 4), np.float32), comb)
+    np.testing.assert_array_equal(new, st[:, perm, :])
+
+
+def test_expand_post_adds_scaled_block():
+    # identity comb: new_i = bf16(post_i * block + state_i), exact in f64 before the rounding
+    s = small_shape(rows=1, act="bf16")
+    st = to_bf(np.random.default_rng(15).standard_normal((1, 4, 64)))
+    block = to_bf(np.random.default_rng(16).standard_normal((1, 64)))
+    post = np.array([[0.5, 1.0, 1.5, 2.0]], np.float32)
+    comb = np.eye(4, dtype=np.float32)[None]
+    new, _ = oracle.expand(s, st, block, post, comb)
+    exp = post[0][:, None].astype(np.float64) * bf(block[0]).astype(np.float64)[None, :] + bf(st[0]).astype(np.float64)
+    np.testing.assert_array_equal(new[0], to_bf(exp))
+
+
 def test_expand_conserves_stream_sum():
     # comb columns sum to 1 => sum_i new_i = sum_j state_j + (sum_i post_i) * block
     cfg = synth.CONFIGS[1]
