@@ -1,0 +1,58 @@
+"""Failure handling of the persistent launch, forced from the host: one workgroup skips its
+arrival at a grid barrier and the wait limit is shortened, so every waiting workgroup's bounded
+wait expires, the error word is set and the launch ends normally (no hang, no fault). After
+mono_workspace_init the workspace works again and gives the same bytes as a fresh one."""
+
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+PH_MIX, PH_ROUTER, PH_GATEUP = 1, 2, 3
+SMALL = synth.CONFIGS[2].with_(hidden=512, n_experts=32, top_k=4, inter=256, shared_inter=256)
+
+
+@pytest.mark.parametrize("phase", [PH_MIX, PH_ROUTER, PH_GATEUP])
+def test_skipped_arrival_times_out_and_recovers(phase):
+    import torch
+    import support
+    import moe_decode_layer_amd as mono
+    print("skipped arrival at barrier", phase, flush=True)
+    g = support.Gpu(SMALL, layers=(0, 1))
+    st = g.state(0)
+    wn = g.layers[1]["w_mix"]
+    ref = g.fused(st, 0, None, wn)
+    grid = mono.mono_grid_size()
+    # 2 ms limit (100 MHz counter); workgroup grid - 1 never arrives at `phase`
+    mono.mono_workspace_set_debug(g.ws, 200000, grid - 1, phase, support.stream())
+    new = g.buf(SMALL.rows * 4 * SMALL.hidden * 2)
+    carry = g.buf(SMALL.rows * 25 * 4)
+    mono.mono_ffn_layer(g.shape, g.structs[0], wn, st, None, new, carry, g.ws, support.stream())
+    status, err = mono.mono_workspace_poll(g.ws, support.stream())
+    assert status == mono.MONO_E_TIMEOUT
+    assert err[0] == 1 and err[1] == phase and 0 <= err[2] < grid
+    assert err[3] == grid   # every workgroup waited at that barrier and gave up once
+    mono.mono_workspace_init(g.ws, g.shape, support.stream())
+    again = g.fused(st, 0, None, wn)
+    support.assert_same(again, ref, ["mixes", "logits", "idx", "weights", "h_routed", "block",
+                                     "new_state", "carry"])
+    del g
+    torch.cuda.empty_cache()
+
+
+def test_short_limit_without_a_fault_still_completes():
+    import torch
+    import support
+    import moe_decode_layer_amd as mono
+    g = support.Gpu(SMALL, layers=(0, 1))
+    st = g.state(1)
+    wn = g.layers[1]["w_mix"]
+    ref = g.fused(st, 0, None, wn)
+    # 20 ms limit is far above any barrier wait of this workload: no expiry
+    mono.mono_workspace_set_debug(g.ws, 2000000, -1, 0, support.stream())
+    out = g.fused(st, 0, None, wn)
+    support.assert_same(out, ref, ["new_state", "carry", "idx"])
+    del g
+    torch.cuda.empty_cache()
