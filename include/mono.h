@@ -132,7 +132,8 @@ mono_status mono_workspace_poll(const void* ws, uint32_t err[4], void* stream);
 
 /* Test hooks (enqueued on `stream`): spin_limit_ticks bounds every device-side wait in units of
  * the 100 MHz real-time counter (0 = default, 2 s); fault_wg / fault_phase make that workgroup
- * skip its arrival at that grid barrier (-1 = off). */
+ * skip its arrival at that synchronisation point (-1 = off): 1 the mix barrier, 2 the store of
+ * its tagged router logit parts, 3 the gate/up barrier. */
 mono_status mono_workspace_set_debug(void* ws, uint32_t spin_limit_ticks, int32_t fault_wg,
                                      int32_t fault_phase, void* stream);
 

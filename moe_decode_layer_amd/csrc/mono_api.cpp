@@ -182,6 +182,7 @@ Params base_params(const mono_shape* s, const mono_layer* L, void* ws, int grid)
   p.ctl = reinterpret_cast<uint32_t*>(b + W.ctl);
   p.mix_part = reinterpret_cast<float*>(b + W.mix_part);
   p.carry_part = reinterpret_cast<float*>(b + W.carry_part);
+  p.lgp = reinterpret_cast<uint64_t*>(b + W.lgp);
   p.trace = reinterpret_cast<uint64_t*>(b + W.trace);
   p.h_routed = b + W.h_routed;
   p.h_shared = b + W.h_shared;
@@ -231,6 +232,10 @@ mono_status mono_workspace_init(void* ws, const mono_shape* shape, void* stream)
   c.ptr(ws, "ws", 256);
   if (c.code != MONO_OK) return c.done();
   Params p = base_params(shape, nullptr, ws, 1);
+  {
+    const WsLayout W = ws_layout(*shape);
+    p.tag_words = (W.lgp_end - W.carry_part) / 8;
+  }
   const int rc = launch(K_WS_INIT, p, shape->act, 0, 0, 1, stream);
   if (rc != 0) {
     g_error = std::string("workspace init: ") + hipGetErrorString((hipError_t)rc);

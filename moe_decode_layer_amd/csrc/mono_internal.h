@@ -97,18 +97,31 @@ struct Params {
   float* carry_ws;   /* workspace copy of the carry */
   /* workspace scratch */
   float* mix_part;   /* [nchunk][R][25] */
-  float* carry_part; /* [nslice][R][25] */
-  uint64_t* trace;   /* [grid][16] real-time stamps */
+  float* carry_part; /* [R * 25][grid] tagged partials: value bits | epoch tag << 32 */
+  uint64_t* lgp;     /* [parts][R][E] tagged router logit parts (same format) */
+  uint64_t* trace;   /* [grid][32] real-time stamps */
+  size_t tag_words; /* u64 words from carry_part through lgp cleared by the workspace init */
   uint32_t* ctl;
 };
 
 /* Workspace layout (byte offsets, 256-byte aligned regions). */
 struct WsLayout {
-  size_t ctl, mix_part, carry_part, mixes, pre, post, comb, x, norm, logits, idx, weights,
+  size_t ctl, mix_part, carry_part, lgp, lgp_end, mixes, pre, post, comb, x, norm, logits, idx, weights,
       h_routed, h_shared, shared, routed, block, carry, trace, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+/* The router splits each f32 row of H values into parts of kRouterCh steps of 256 values; the
+ * parts are computed by different waves and summed by the select in part order. */
+constexpr int kRouterCh = 10;
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline size_t router_parts(size_t H) {
+  const size_t steps = (H + 255) / 256;
+  return (steps + kRouterCh - 1) / kRouterCh;
+}
 
 /* Phase timestamps per workgroup in the trace region. */
 constexpr int kTraceSlots = 32;
@@ -127,7 +140,9 @@ inline WsLayout ws_layout(const mono_shape& s) {
   };
   L.ctl = take(CTL_WORDS * 4);
   L.mix_part = take(nchunk * R * kNCarry * 4);
-  L.carry_part = take((size_t)kMaxGrid * R * kNCarry * 4);
+  L.carry_part = take((size_t)kMaxGrid * R * kNCarry * 8);
+  L.lgp = take(router_parts(s.hidden) * R * E * 8);
+  L.lgp_end = o;
   L.mixes = take(R * kNMix * 4);
   L.pre = take(R * 4 * 4);
   L.post = take(R * 4 * 4);

@@ -45,6 +45,7 @@ constexpr int kMaxUnion = kMaxRows * kMaxTopK;
 constexpr int kRG = 4; /* consecutive down-projection rows per task */
 constexpr int kMaxStaged = 160; /* hidden rows staged at once (80 KB / 512 B at least) */
 constexpr uint32_t kHidShared = 0x80000000u;
+constexpr int kSliceMax = 32; /* hidden positions per workgroup whose expand inputs sit in LDS */
 
 /* ------------------------------------------------------------------------------------------
  * Number formats */
@@ -145,8 +146,39 @@ __device__ __forceinline__ uint4 coh_b128(__amdgpu_buffer_rsrc_t r, uint32_t off
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+__device__ __forceinline__ uint2 coh_b64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const v2u_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kCohPolicy);
+  return make_uint2(v[0], v[1]);
+}
+
 /* Waits until this wave's memory operations have completed (and orders the compiler). */
 __device__ __forceinline__ void drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+/* Copies `bytes` (a multiple of 4) of device-coherent global memory at `src` into LDS at `dst`
+ * with the whole workgroup: 16-byte loads, up to 8 per thread in flight before they are stored,
+ * then 4-byte loads for a tail. The caller synchronises before reading dst. */
+__device__ __forceinline__ void coh_copy_to_lds(const void* src, size_t bytes, uint8_t* dst) {
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t r = coh_region(src, bytes);
+  const int n16 = (int)(bytes / 16);
+  constexpr int B = 8;
+  for (int v0 = 0; v0 < n16; v0 += B * kBlock) {
+    uint4 buf[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int v = v0 + b * kBlock + tid;
+      if (v < n16) buf[b] = coh_b128(r, (uint32_t)v * 16u);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int v = v0 + b * kBlock + tid;
+      if (v < n16) reinterpret_cast<uint4*>(dst)[v] = buf[b];
+    }
+  }
+  const int t = n16 * 4 + tid;
+  if (t < (int)(bytes / 4))
+    reinterpret_cast<float*>(dst)[t] = coh_f32(r, (uint32_t)t * 4u);
+}
 
 /* ------------------------------------------------------------------------------------------
  * Wave reductions (DPP butterflies inside each row of 16 lanes, then the four row sums). Must
@@ -192,6 +224,7 @@ __host__ __device__ constexpr size_t row_sbytes(int fmt, size_t k) {
   return fmt == Q8 ? (k / 32) * 2 : fmt == FP4 ? k / 32 : 0;
 }
 
+/* Loads step s of a row of K elements for this lane (zeros past the end of the row). */
 template <int FMT>
 __device__ __forceinline__ void wload(const uint8_t* vrow, const uint8_t* srow, int s, int lane,
                                       int K, uint4& v, uint32_t& sc) {
@@ -244,6 +277,7 @@ __device__ __forceinline__ void decode(const uint4& v, uint32_t sc, uint32_t (&w
 }
 
 /* acc + scale * (pairs . bf16 activations k .. k + 2 PAIRS - 1 of one LDS row). */
+/* acc + scale * (weight pairs . activations[k, k + EL)) for one lane. */
 template <int FMT>
 __device__ __forceinline__ float dot_pairs(const uint32_t (&w)[Fmt<FMT>::PAIRS], float scale,
                                            const void* arow, int k, float acc) {
@@ -306,7 +340,8 @@ __device__ __forceinline__ void wregs_load(WRegs<FMT, NR, CH>& W, const uint8_t*
     }
 }
 
-/* acc[m][r] += (chunk of row m) . act_r for every r in `mask` (per-lane partials). */
+/* acc[m][r] += (chunk of row m) . act_r for every r in `mask` (per-lane partials); with one
+ * row every task row is used, so the row test is dropped. */
 template <int FMT, int ACT, int RMAX, int NR, int CH>
 __device__ __forceinline__ void wregs_dot(const WRegs<FMT, NR, CH>& W, int K, int s0,
                                           const void* const (&arow)[RMAX], uint32_t mask,
@@ -323,14 +358,14 @@ __device__ __forceinline__ void wregs_dot(const WRegs<FMT, NR, CH>& W, int K, in
         if constexpr (FMT == F32) {
 #pragma unroll
           for (int r = 0; r < RMAX; ++r)
-            if (mask & (1u << r)) acc[m][r] = dot_f32(W.v[m][c], arow[r], k, acc[m][r]);
+            if (RMAX == 1 || (mask & (1u << r))) acc[m][r] = dot_f32(W.v[m][c], arow[r], k, acc[m][r]);
         } else {
           uint32_t w[Fmt<FMT>::PAIRS];
           float scale;
           decode<FMT>(W.v[m][c], W.sc[m][c], w, scale);
 #pragma unroll
           for (int r = 0; r < RMAX; ++r)
-            if (mask & (1u << r)) acc[m][r] = dot_pairs<FMT>(w, scale, arow[r], k, acc[m][r]);
+            if (RMAX == 1 || (mask & (1u << r))) acc[m][r] = dot_pairs<FMT>(w, scale, arow[r], k, acc[m][r]);
         }
       }
     }
@@ -379,12 +414,17 @@ struct Smem {
   uint16_t vdst[kMaxStaged]; /* LDS offset in 16 B, */
   uint16_t vlen[kMaxStaged]; /* length in 16 B */
   int nv;
+  int sel_ok;      /* cleared when a select wave's logits did not arrive */
+  int shared_next; /* next shared-expert gate/up task of this workgroup (fused launch) */
   int nU;
   int flag;
   uint64_t epoch;
   int trace_on;
   int state_in_lds;
   float bias[kMaxExperts];
+  float wnext[kNMix * 4 * kSliceMax]; /* next mix weights of the slice [24][4][hs] */
+  float sslice[kMaxRows * 4 * kSliceMax]; /* input state of the slice [R][4][hs] */
+  float cred[kMaxGrid];                  /* carry reduction: one partial per workgroup */
   uint32_t spin;
   int skip_phase;
 };
@@ -467,34 +507,6 @@ __device__ __forceinline__ bool bar_wait(const Params& p, Smem& sm, int phase) {
       }
     }
     if (lane == 0) sm.flag = ok;
-  }
-  __syncthreads();
-  return sm.flag != 0;
-}
-
-/* Arrival at the end counters (every workgroup of every fused launch arrives once) that tells
- * the caller whether this workgroup may sum the carry partials: it completed its own group and
- * then found every other group complete. The last increment overall always qualifies; if two
- * qualify they write identical values. All threads get the answer. */
-__device__ __forceinline__ bool arrive_last(const Params& p, Smem& sm) {
-  drain();
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int mine = blockIdx.x % kBarGroups;
-    uint64_t v = 0;
-    if (lane == 0)
-      v = __hip_atomic_fetch_add(bar_counter(p, PH_END, mine), (uint64_t)1, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT) + 1;
-    const uint64_t mine_now = __shfl(v, 0);
-    const int g = lane < kBarGroups ? lane : 0;
-    uint64_t c = 0;
-    if (lane < kBarGroups && lane != mine) c = ld_coh(bar_counter(p, PH_END, g));
-    if (lane == mine) c = mine_now;
-    const bool done = lane >= kBarGroups || c >= bar_target(sm, g);
-    const bool all = __ballot(!done) == 0ull;
-    const bool own_last = mine_now == bar_target(sm, mine);
-    if (lane == 0) sm.flag = (all && own_last) ? 1 : 0;
   }
   __syncthreads();
   return sm.flag != 0;
@@ -617,37 +629,22 @@ __device__ __forceinline__ void ph_hc_pre(const Params& p, Smem& sm, bool write_
   const int R = p.R, H = p.H, n = 4 * H, nch = n / kMixChunk;
   constexpr int VE = ACT == F32 ? 4 : 8; /* elements per 16-byte state load */
   const size_t ab = ACT == F32 ? 4 : 2;
-  /* raw mix sums: one wave per (row, output); lanes take chunks t = lane + 64 m; the loads of
-   * up to 8 sums are issued before any is reduced */
-  constexpr int PB = 8;
-  const __amdgpu_buffer_rsrc_t part = coh_region(p.mix_part, (size_t)nch * R * kNCarry * 4);
-  for (int q0 = wave; q0 < R * kNCarry; q0 += kWaves * PB) {
-    float v[PB];
-#pragma unroll
-    for (int b = 0; b < PB; ++b) v[b] = 0.0f;
-    for (int t0 = 0; t0 < nch; t0 += 64) {
-      const int t = t0 + lane;
-#pragma unroll
-      for (int b = 0; b < PB; ++b) {
-        const int q = q0 + b * kWaves;
-        if (q < R * kNCarry) {
-          const int r = q / kNCarry, j = q % kNCarry;
-          if (p.carry_in) {
-            if (t == 0) v[b] += p.carry_in[r * kNCarry + j];
-          } else if (t < nch) {
-            v[b] += coh_f32(part, (uint32_t)((((size_t)t * R + r) * kNCarry + j) * 4));
-          }
-        }
-      }
+  /* raw mix sums: the partials [chunk][row][25] are copied into LDS with contiguous 16-byte
+   * coherent loads (one pass over 8 KB per row), then one wave per (row, output) sums them,
+   * lanes taking chunks t = lane + 64 m */
+  float* part = reinterpret_cast<float*>(sm.big); /* free until x is written below */
+  if (!p.carry_in) coh_copy_to_lds(p.mix_part, (size_t)nch * R * kNCarry * 4, sm.big);
+  __syncthreads();
+  for (int q = wave; q < R * kNCarry; q += kWaves) {
+    const int r = q / kNCarry, j = q % kNCarry;
+    float v = 0.0f;
+    if (p.carry_in) {
+      if (lane == 0) v = p.carry_in[r * kNCarry + j];
+    } else {
+      for (int t = lane; t < nch; t += 64) v += part[((size_t)t * R + r) * kNCarry + j];
     }
-#pragma unroll
-    for (int b = 0; b < PB; ++b) {
-      const int q = q0 + b * kWaves;
-      if (q < R * kNCarry) {
-        const float tot = wave_sum(v[b]);
-        if (lane == 0) sm.raw[q / kNCarry][q % kNCarry] = tot;
-      }
-    }
+    const float tot = wave_sum(v);
+    if (lane == 0) sm.raw[r][j] = tot;
   }
   __syncthreads();
   stamp(p, sm.trace_on != 0, 14);
@@ -849,72 +846,158 @@ __device__ __forceinline__ void act_rows_ptrs(const Params& p, const Smem& sm,
  * Phase: router logits [ds4 router commit: the F32 logits matvec]. One wave per expert row,
  * rows spread over compute units first; the fused launch loads each wave's first row before
  * the mix barrier. */
-typedef WRegs<F32, 1, 20> RouterRegs;
+typedef WRegs<F32, 1, kRouterCh> RouterRegs;
 
 /* Issues the loads of this wave's first router row chunk (task order of ph_router). */
+/* Router task of this wave. A row of H values splits into P parts of kRouterCh steps; when
+ * ceil(E / grid) * P <= 7, expert e goes to workgroup e % grid and its parts to waves 1, 2, ...
+ * there (the select sums the parts in part order), so every wave holds at most one part in
+ * flight.
+ * Otherwise (local == false) each wave walks whole rows e = wave_major_id() + n * waves. In the
+ * local case wave 0 has no router part, so its barrier polls do not queue behind early loads. */
+struct RouterTask {
+  bool local;
+  int P, e, part;
+};
+
+__device__ __forceinline__ RouterTask router_task(const Params& p) {
+  RouterTask t;
+  const int nsteps = (p.H + 255) / 256;
+  t.P = (nsteps + kRouterCh - 1) / kRouterCh;
+  const int per = (p.E + (int)gridDim.x - 1) / (int)gridDim.x;
+  t.local = per * t.P <= kWaves - 1;
+  const int wave = threadIdx.x >> 6;
+  if (t.local) {
+    /* waves 1.. take the parts; wave 0 (which polls the barriers) loads nothing early */
+    const int j = (wave - 1) / t.P;
+    t.part = (wave - 1) % t.P;
+    t.e = wave > 0 && j < per ? (int)blockIdx.x + j * (int)gridDim.x : p.E;
+  } else {
+    t.part = 0;
+    t.e = wave_major_id();
+  }
+  return t;
+}
+
+/* Issues the loads of this wave's first router chunk (the task order of ph_router). */
 __device__ __forceinline__ void router_prefetch(const Params& p, RouterRegs& W) {
-  const int e = wave_major_id();
-  if (e < p.E) {
-    const uint8_t* vr[1] = {reinterpret_cast<const uint8_t*>(p.w_router + (size_t)e * p.H)};
+  const RouterTask t = router_task(p);
+  if (t.e < p.E) {
+    const uint8_t* vr[1] = {reinterpret_cast<const uint8_t*>(p.w_router + (size_t)t.e * p.H)};
     const uint8_t* sr[1] = {nullptr};
-    wregs_load(W, vr, sr, p.H, 0);
+    wregs_load(W, vr, sr, p.H, t.part * kRouterCh);
   }
 }
 
-template <int ACT, int RMAX, bool PRE>
-__device__ __forceinline__ void ph_router(const Params& p, const Smem& sm, const RouterRegs& pre) {
+/* acc[r] += kRouterCh steps of one f32 router row (in W, from step s0) . act row r. */
+template <int ACT, int RMAX>
+__device__ __forceinline__ void router_dot(const RouterRegs& W, int s0, int H, bool whole,
+                                           const void* const (&arow)[RMAX], uint32_t mask,
+                                           float (&acc)[RMAX]) {
+  constexpr int EL = 4;
   const int lane = threadIdx.x & 63;
-  const int nwt = gridDim.x * kWaves;
+#pragma unroll
+  for (int c = 0; c < kRouterCh; ++c) {
+    int k = ((s0 + c) * 64 + lane) * EL;
+    const bool valid = whole || k < H;
+    k = min(k, H - EL);
+    const float w0 = valid ? __uint_as_float(W.v[0][c].x) : 0.0f;
+    const float w1 = valid ? __uint_as_float(W.v[0][c].y) : 0.0f;
+    const float w2 = valid ? __uint_as_float(W.v[0][c].z) : 0.0f;
+    const float w3 = valid ? __uint_as_float(W.v[0][c].w) : 0.0f;
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      if (RMAX > 1 && !(mask & (1u << r))) continue;
+      float x0, x1, x2, x3;
+      if constexpr (ACT == F32) {
+        const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(arow[r]) + k);
+        x0 = x.x; x1 = x.y; x2 = x.z; x3 = x.w;
+      } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(arow[r]) + k);
+        x0 = bf2f(x.x & 0xFFFFu); x1 = bf2f(x.x >> 16);
+        x2 = bf2f(x.y & 0xFFFFu); x3 = bf2f(x.y >> 16);
+      }
+      float a = acc[r];
+      a = fmaf(w0, x0, a);
+      a = fmaf(w1, x1, a);
+      a = fmaf(w2, x2, a);
+      a = fmaf(w3, x3, a);
+      acc[r] = a;
+    }
+  }
+}
+
+/* Tagged store of one router logit part: value bits in the low word, tag in the high word. */
+__device__ __forceinline__ void store_logit_part(const Params& p, int part, int r, int e, float v,
+                                                 uint32_t tag) {
+  st_coh(p.lgp + ((size_t)part * p.R + r) * p.E + e, ((uint64_t)tag << 32) | __float_as_uint(v));
+}
+
+/* Every (expert, part) task stores its partial dot products as tagged values (tag = the launch
+ * epoch + 1 in the fused launch, 0 otherwise); the select waits for the tags, so no grid
+ * barrier separates the router from the select. With skip (fault injection) nothing is
+ * stored. */
+template <int ACT, int RMAX, bool PRE>
+__device__ __forceinline__ void ph_router(const Params& p, Smem& sm, const RouterRegs& pre,
+                                          uint32_t tag, bool skip) {
+  const int lane = threadIdx.x & 63;
   const void* arow[RMAX];
   act_rows_ptrs<ACT, RMAX>(p, sm, arow);
   const uint32_t mask = (1u << p.R) - 1u;
   constexpr int EL = 4;
   const int nsteps = (p.H + 64 * EL - 1) / (64 * EL);
-  for (int e = wave_major_id(); e < p.E; e += nwt) {
-    const uint8_t* vr[1] = {reinterpret_cast<const uint8_t*>(p.w_router + (size_t)e * p.H)};
-    const uint8_t* sr[1] = {nullptr};
+  const bool whole = p.H % (64 * EL * kRouterCh) == 0;
+  const RouterTask t = router_task(p);
+  stamp(p, sm.trace_on != 0, 22);
+  if (t.local) {
     float acc[RMAX];
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) acc[r] = 0.0f;
-    for (int s0 = 0; s0 < nsteps; s0 += 20) {
-      RouterRegs W;
-      if (PRE && s0 == 0 && e == wave_major_id())
-        W = pre;
-      else
+    if (t.e < p.E) {
+      const int s0 = t.part * kRouterCh;
+      if (PRE) {
+        router_dot<ACT, RMAX>(pre, s0, p.H, whole, arow, mask, acc);
+      } else {
+        const uint8_t* vr[1] = {reinterpret_cast<const uint8_t*>(p.w_router + (size_t)t.e * p.H)};
+        const uint8_t* sr[1] = {nullptr};
+        RouterRegs W;
         wregs_load(W, vr, sr, p.H, s0);
-#pragma unroll
-      for (int c = 0; c < 20; ++c) {
-        const int k = ((s0 + c) * 64 + lane) * EL;
-        if (s0 + c < nsteps && k < p.H) {
-#pragma unroll
-          for (int r = 0; r < RMAX; ++r) {
-            if (!(mask & (1u << r))) continue;
-            float x0, x1, x2, x3;
-            if constexpr (ACT == F32) {
-              const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(arow[r]) + k);
-              x0 = x.x; x1 = x.y; x2 = x.z; x3 = x.w;
-            } else {
-              const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(arow[r]) + k);
-              x0 = bf2f(x.x & 0xFFFFu); x1 = bf2f(x.x >> 16);
-              x2 = bf2f(x.y & 0xFFFFu); x3 = bf2f(x.y >> 16);
-            }
-            float a = acc[r];
-            a = fmaf(__uint_as_float(W.v[0][c].x), x0, a);
-            a = fmaf(__uint_as_float(W.v[0][c].y), x1, a);
-            a = fmaf(__uint_as_float(W.v[0][c].z), x2, a);
-            a = fmaf(__uint_as_float(W.v[0][c].w), x3, a);
-            acc[r] = a;
-          }
-        }
+        router_dot<ACT, RMAX>(W, s0, p.H, whole, arow, mask, acc);
       }
     }
+    stamp(p, sm.trace_on != 0, 23);
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
       if (r >= p.R) break;
-      const float t = wave_sum(acc[r]);
-      if (lane == 0) stf_coh(p.logits + (size_t)r * p.E + e, t);
+      const float v = wave_sum(acc[r]);
+      if (lane == 0 && t.e < p.E && !skip) store_logit_part(p, t.part, r, t.e, v, tag);
+    }
+    return;
+  }
+  const int nwt = gridDim.x * kWaves;
+  for (int e = wave_major_id(); e < p.E; e += nwt) {
+    const uint8_t* vr[1] = {reinterpret_cast<const uint8_t*>(p.w_router + (size_t)e * p.H)};
+    const uint8_t* sr[1] = {nullptr};
+    for (int q = 0; q < t.P; ++q) {
+      float part[RMAX];
+#pragma unroll
+      for (int r = 0; r < RMAX; ++r) part[r] = 0.0f;
+      if (PRE && q == 0 && e == wave_major_id()) {
+        router_dot<ACT, RMAX>(pre, 0, p.H, whole, arow, mask, part);
+      } else {
+        RouterRegs W;
+        wregs_load(W, vr, sr, p.H, q * kRouterCh);
+        router_dot<ACT, RMAX>(W, q * kRouterCh, p.H, whole, arow, mask, part);
+      }
+#pragma unroll
+      for (int r = 0; r < RMAX; ++r) {
+        if (r >= p.R) break;
+        const float v = wave_sum(part[r]);
+        if (lane == 0 && !skip) store_logit_part(p, q, r, e, v, tag);
+      }
     }
   }
+  (void)nsteps;
 }
 
 /* ------------------------------------------------------------------------------------------
@@ -933,96 +1016,185 @@ __device__ __forceinline__ uint32_t ord_f32(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int CTRL>
-__device__ __forceinline__ void key_max_step(uint32_t& hi, uint32_t& lo) {
-  const uint32_t oh = dpp_u<CTRL>(hi), ol = dpp_u<CTRL>(lo);
-  const bool take = oh > hi || (oh == hi && ol > lo);
-  hi = take ? oh : hi;
-  lo = take ? ol : lo;
+/* softplus(z) = max(z, 0) + log1p(exp(-|z|)) in f32. log1p(t) for t in (0, 1] uses the
+ * correction log(u) * t / (u - 1) with u = 1 + t rounded (exact where u == 1: log1p(t) = t to
+ * f32 precision), which keeps the relative error near that of log. */
+__device__ __forceinline__ float softplus_f32(float z) {
+  const float t = expf(-fabsf(z));
+  const float u = 1.0f + t;
+  const float l = u == 1.0f ? t : __logf(u) * (t / (u - 1.0f));
+  return fmaxf(z, 0.0f) + l;
 }
 
-template <int CTRL, int ROWS>
-__device__ __forceinline__ void key_max_bcast(uint32_t& hi, uint32_t& lo) {
-  /* lanes of rows outside ROWS keep their own value (old = src) */
-  const uint32_t oh = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROWS, 0xF, false);
-  const uint32_t ol = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROWS, 0xF, false);
-  const bool take = oh > hi || (oh == hi && ol > lo);
-  hi = take ? oh : hi;
-  lo = take ? ol : lo;
+/* Largest unsigned value over the wave, uniform. */
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<0xB1>(v));
+  v = max(v, dpp_u<0x4E>(v));
+  v = max(v, dpp_u<0x141>(v));
+  v = max(v, dpp_u<0x140>(v));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-/* Largest 64-bit key (hi, lo) over the wave, returned (uniform) to every lane: butterflies
- * inside each 16-lane row, then row broadcasts carry the maxima to the last row. */
-__device__ __forceinline__ uint64_t wave_max_key(uint32_t hi, uint32_t lo) {
-  key_max_step<0xB1>(hi, lo);
-  key_max_step<0x4E>(hi, lo);
-  key_max_step<0x141>(hi, lo);
-  key_max_step<0x140>(hi, lo);
-  key_max_bcast<0x142, 0xA>(hi, lo); /* row_bcast:15 into rows 1 and 3 */
-  key_max_bcast<0x143, 0xC>(hi, lo); /* row_bcast:31 into rows 2 and 3 */
-  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 63) << 32) |
-         (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
+/* Compare-exchange of two (hi, lo, s) entries so that entry a holds the larger key. */
+__device__ __forceinline__ void key_cx(uint32_t& ah, uint32_t& al, float& as, uint32_t& bh,
+                                       uint32_t& bl, float& bs) {
+  const bool sw = bh > ah || (bh == ah && bl > al);
+  const uint32_t th = sw ? bh : ah, tl = sw ? bl : al;
+  const float ts = sw ? bs : as;
+  bh = sw ? ah : bh;
+  bl = sw ? al : bl;
+  bs = sw ? as : bs;
+  ah = th;
+  al = tl;
+  as = ts;
 }
 
+/* Top-k of one row by the 64-bit key (ord(s + bias) << 32) | ~e: biased score descending, then
+ * expert index ascending [ds4 page, tie-order commit]. Each lane sorts its PER candidates once;
+ * a round takes the largest head over the wave (high word, then low word among the lanes that
+ * hold it) and the owning lane pops its head. */
+/* Logits of row r for this lane's experts e = lane + 64 c: the sum of the router's parts in
+ * part order. With check, waits (bounded) until every part carries `tag`; returns false on
+ * expiry (uniform over the wave). */
 template <int PER>
-__device__ __forceinline__ void select_row(const Params& p, Smem& sm, int r) {
-  const int lane = threadIdx.x & 63, E = p.E, K = p.K;
-  const __amdgpu_buffer_rsrc_t lg = coh_region(p.logits, (size_t)p.R * E * 4);
-  uint32_t khi[PER], klo[PER];
-  float sv[PER], zs[PER], bs[PER];
+__device__ __forceinline__ bool gather_logits(const Params& p, const Smem& sm, int r, bool check,
+                                              uint32_t tag, float (&z)[PER]) {
+  const int lane = threadIdx.x & 63, E = p.E;
+  const int P = (int)router_parts(p.H);
+  const __amdgpu_buffer_rsrc_t lg = coh_region(p.lgp, (size_t)P * p.R * E * 8);
 #pragma unroll
-  for (int c = 0; c < PER; ++c) {
-    const int e = lane + 64 * c;
-    zs[c] = coh_f32(lg, (uint32_t)(((size_t)r * E + e) * 4));
-    bs[c] = e < E ? sm.bias[e] : 0.0f;
+  for (int c = 0; c < PER; ++c) z[c] = 0.0f;
+  bool ok = true;
+  for (int q0 = 0; q0 < P; q0 += 2) {
+    uint2 v[PER][2];
+    bool need[PER][2];
+#pragma unroll
+    for (int c = 0; c < PER; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = lane + 64 * c, q = q0 + h;
+        need[c][h] = e < E && q < P;
+        v[c][h] = make_uint2(0u, tag);
+        if (need[c][h]) v[c][h] = coh_b64(lg, (uint32_t)((((size_t)q * p.R + r) * E + e) * 8));
+      }
+    if (check) {
+      auto pending = [&]() {
+        bool any = false;
+#pragma unroll
+        for (int c = 0; c < PER; ++c)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) any |= need[c][h] && v[c][h].y != tag;
+        return any;
+      };
+      if (__ballot(pending()) != 0ull) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (__ballot(pending()) != 0ull) {
+          __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+          for (int c = 0; c < PER; ++c)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              if (need[c][h] && v[c][h].y != tag)
+                v[c][h] = coh_b64(lg, (uint32_t)((((size_t)(q0 + h) * p.R + r) * E + lane + 64 * c) * 8));
+          if (__builtin_amdgcn_s_memrealtime() - t0 > sm.spin) {
+            ok = false;
+            break;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < PER; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (need[c][h]) z[c] += __uint_as_float(v[c][h].x);
   }
+  return ok;
+}
+
+/* Top-k of one row by the 64-bit key (ord(s + bias) << 32) | ~e: biased score descending, then
+ * expert index ascending [ds4 page, tie-order commit]. Each lane sorts its PER candidates once;
+ * a round takes the largest head over the wave (high word, then low word among the lanes that
+ * hold it) and the owning lane pops its head. Returns false when the logits did not arrive. */
+template <int PER>
+__device__ __forceinline__ bool select_row(const Params& p, Smem& sm, int r, bool write_out,
+                                           bool check, uint32_t tag) {
+  const int lane = threadIdx.x & 63, E = p.E, K = p.K;
+  uint32_t kh[PER], kl[PER];
+  float sv[PER], zs[PER];
+  if (!gather_logits<PER>(p, sm, r, check, tag, zs)) return false;
+  stamp(p, sm.trace_on != 0, 24);
 #pragma unroll
   for (int c = 0; c < PER; ++c) {
     const int e = lane + 64 * c;
-    khi[c] = 0u;
-    klo[c] = 0u;
+    kh[c] = 0u;
+    kl[c] = 0u;
     sv[c] = 0.0f;
     if (e < E) {
       const float z = zs[c];
-      const float sp = z > 0.0f ? z + log1pf(expf(-z)) : log1pf(expf(z));
-      const float sc = sqrtf(sp);
-      khi[c] = ord_f32(sc + bs[c]);
-      klo[c] = 0xFFFFFFFFu - (uint32_t)e;
+      if (write_out) p.logits[(size_t)r * E + e] = z;
+      const float sc = sqrtf(softplus_f32(z));
+      kh[c] = ord_f32(sc + sm.bias[e]);
+      kl[c] = 0xFFFFFFFFu - (uint32_t)e;
       sv[c] = sc;
     }
   }
   stamp(p, sm.trace_on != 0, 19);
+  /* odd-even transposition sort, descending */
+#pragma unroll
+  for (int ph = 0; ph < PER; ++ph)
+#pragma unroll
+    for (int c = ph & 1; c + 1 < PER; c += 2)
+      key_cx(kh[c], kl[c], sv[c], kh[c + 1], kl[c + 1], sv[c + 1]);
   for (int j = 0; j < K; ++j) {
-    uint32_t bh = 0u, bl = 0u;
-#pragma unroll
-    for (int c = 0; c < PER; ++c) {
-      const bool take = khi[c] > bh || (khi[c] == bh && klo[c] > bl);
-      bh = take ? khi[c] : bh;
-      bl = take ? klo[c] : bl;
+    const uint32_t mh = wave_max_u32(kh[0]);
+    const uint32_t ml = wave_max_u32(kh[0] == mh ? kl[0] : 0u);
+    const bool win = kh[0] == mh && kl[0] == ml;
+    const uint64_t who = __ballot(win);
+    const float s_win = readlane(sv[0], (int)__builtin_ctzll(who));
+    if (lane == 0) {
+      sm.sel_e[r][j] = (int)(0xFFFFFFFFu - ml);
+      sm.sel_s[r][j] = s_win;
     }
-    const uint64_t best = wave_max_key(bh, bl);
-    const uint32_t wh = (uint32_t)(best >> 32), wl = (uint32_t)best;
+    if (win) {
 #pragma unroll
-    for (int c = 0; c < PER; ++c) {
-      if (klo[c] == wl && khi[c] == wh && lane + 64 * c < E) {
-        sm.sel_e[r][j] = (int)(0xFFFFFFFFu - wl);
-        sm.sel_s[r][j] = sv[c];
-        khi[c] = 0u;
-        klo[c] = 0u;
+      for (int c = 0; c + 1 < PER; ++c) {
+        kh[c] = kh[c + 1];
+        kl[c] = kl[c + 1];
+        sv[c] = sv[c + 1];
       }
+      kh[PER - 1] = 0u;
+      kl[PER - 1] = 0u;
+      sv[PER - 1] = 0.0f;
     }
+  }
+  return true;
+}
+
+/* Select, part 1: waves 0 .. min(R, 8) - 1 take rows r = wave, wave + 8, ... Needs sm.sel_ok
+ * set to 1 beforehand (made visible by a __syncthreads); no workgroup barrier inside, so other
+ * waves may do independent work meanwhile. */
+__device__ __forceinline__ void select_rows(const Params& p, Smem& sm, bool write_out, bool check,
+                                            uint32_t tag) {
+  const int wave = threadIdx.x >> 6;
+  for (int r = wave; r < p.R; r += kWaves) {
+    const bool ok = p.E <= 256 ? select_row<4>(p, sm, r, write_out, check, tag)
+                               : select_row<kMaxExperts / 64>(p, sm, r, write_out, check, tag);
+    if (!ok && (threadIdx.x & 63) == 0) sm.sel_ok = 0;
   }
 }
 
-__device__ __forceinline__ void ph_select(const Params& p, Smem& sm, bool write_out) {
-  const int tid = threadIdx.x, wave = tid >> 6, K = p.K;
-  for (int r = wave; r < p.R; r += kWaves) {
-    if (p.E <= 256)
-      select_row<4>(p, sm, r);
-    else
-      select_row<kMaxExperts / 64>(p, sm, r); /* 8 candidates per lane */
+/* Select, part 2 (after a __syncthreads that follows part 1): normalised, clamped and scaled
+ * routing weights. Returns false (after reporting once) when some row's logits did not arrive
+ * in time. */
+__device__ __forceinline__ bool select_finish(const Params& p, Smem& sm, bool write_out) {
+  const int tid = threadIdx.x, K = p.K;
+  if (sm.sel_ok == 0) {
+    if (tid == 0) report_timeout(p, PH_ROUTER);
+    return false;
   }
-  __syncthreads();
   if (tid < p.R) {
     const int r = tid;
     float sum = 0.0f;
@@ -1038,6 +1210,16 @@ __device__ __forceinline__ void ph_select(const Params& p, Smem& sm, bool write_
     }
   }
   __syncthreads();
+  return true;
+}
+
+__device__ __forceinline__ bool ph_select(const Params& p, Smem& sm, bool write_out, bool check,
+                                          uint32_t tag) {
+  if (threadIdx.x == 0) sm.sel_ok = 1;
+  __syncthreads();
+  select_rows(p, sm, write_out, check, tag);
+  __syncthreads();
+  return select_finish(p, sm, write_out);
 }
 
 /* Reads a caller-provided selection (idx, weights) into sm.sel_*; indices are clamped into
@@ -1143,6 +1325,24 @@ __device__ __forceinline__ void ph_gateup_shared(const Params& p, const Smem& sm
   const uint32_t mask = (1u << p.R) - 1u;
   for (int i = wave_major_id(); i < p.Is; i += nwt)
     gateup_task<ACT, SFMT, RMAX>(p, sm, p.shared, 0, i, p.Is, mask, 0, true);
+}
+
+/* Shared-expert gate/up in the fused launch: workgroup g owns rows g, g + grid, ...; its waves
+ * claim them one at a time from an LDS counter (sm.shared_next, zeroed beforehand), so a wave
+ * that also selects joins when it is done. */
+template <int ACT, int SFMT, int RMAX>
+__device__ __forceinline__ void ph_gateup_shared_claim(const Params& p, Smem& sm) {
+  if (p.Is <= 0) return;
+  const uint32_t mask = (1u << p.R) - 1u;
+  for (;;) {
+    /* all 64 lanes add 1 and lane 0's old value (a multiple of 64) is read back uniformly: no
+     * divergent branch in the loop, so every lane stays in the same iteration and they leave
+     * together */
+    const int n = __builtin_amdgcn_readfirstlane(atomicAdd(&sm.shared_next, 1)) / 64;
+    const int i = (int)blockIdx.x + n * (int)gridDim.x;
+    if (i >= p.Is) break;
+    gateup_task<ACT, SFMT, RMAX>(p, sm, p.shared, 0, i, p.Is, mask, 0, true);
+  }
 }
 
 /* Routed gate/up: the nU * I tasks split into equal contiguous ranges, one per wave. */
@@ -1254,6 +1454,151 @@ __device__ __forceinline__ int down_group_end(const Params& p, const Smem& sm, i
   return item;
 }
 
+/* Hidden-position slice of the workgroup for the down projections and the expand. */
+struct Slice {
+  int h0, nh, hs;
+  bool lds; /* the slice's state and next mix weights were copied into LDS */
+};
+
+__device__ __forceinline__ Slice slice_of(const Params& p) {
+  Slice c;
+  c.hs = (p.H + p.nslice - 1) / p.nslice;
+  c.h0 = blockIdx.x * c.hs;
+  c.nh = p.H - c.h0 < c.hs ? p.H - c.h0 : c.hs;
+  if (c.nh < 0) c.nh = 0;
+  c.lds = c.hs <= kSliceMax;
+  return c;
+}
+
+/* Loads of the slice's input state [R][4][nh] and next mix weights [24][4][nh] into registers
+ * (issued early so that their latency overlaps other waiting), then stored into LDS by
+ * slice_store. Element e of the flat list: state first, then weights. */
+constexpr int kSliceRegs = (kMaxRows * 4 * kSliceMax + kNMix * 4 * kSliceMax + kBlock - 1) / kBlock;
+struct SliceRegs {
+  float v[kSliceRegs];
+};
+
+template <int ACT>
+__device__ __forceinline__ void slice_prefetch(const Params& p, const Slice& c, SliceRegs& sr) {
+  if (!c.lds) return;
+  const int tid = threadIdx.x, nh = c.nh, H = p.H;
+  const int ns = p.R * 4 * nh, nw = p.w_mix_next ? kNMix * 4 * nh : 0;
+#pragma unroll
+  for (int k = 0; k < kSliceRegs; ++k) {
+    const int e = tid + k * kBlock;
+    sr.v[k] = 0.0f;
+    if (e < ns) {
+      const int hl = e % nh, ri = e / nh; /* ri = r * 4 + i */
+      sr.v[k] = act_ld<ACT>(p.state, (size_t)ri * H + c.h0 + hl);
+    } else if (e < ns + nw) {
+      const int f = e - ns, hl = f % nh, ji = f / nh; /* ji = j * 4 + i */
+      sr.v[k] = p.w_mix_next[(size_t)ji * H + c.h0 + hl];
+    }
+  }
+}
+
+__device__ __forceinline__ void slice_store(const Params& p, const Slice& c, Smem& sm,
+                                            const SliceRegs& sr) {
+  if (!c.lds) return;
+  const int tid = threadIdx.x, nh = c.nh;
+  const int ns = p.R * 4 * nh, nw = p.w_mix_next ? kNMix * 4 * nh : 0;
+#pragma unroll
+  for (int k = 0; k < kSliceRegs; ++k) {
+    const int e = tid + k * kBlock;
+    if (e < ns)
+      sm.sslice[(e / nh) * kSliceMax + e % nh] = sr.v[k];
+    else if (e < ns + nw)
+      sm.wnext[((e - ns) / nh) * kSliceMax + (e - ns) % nh] = sr.v[k];
+  }
+}
+
+/* Staging list of the items [first, last): for every (item, row that uses it), in item-major
+ * order, the source of the hidden row (routed [R][K][I] or shared [R][Is]), its LDS offset and
+ * length in 16-byte units, and sm.voff. One wave scans the items 64 at a time. */
+__device__ __forceinline__ void stage_list(const Params& p, Smem& sm, int first, int last,
+                                           size_t ab) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x, nU = sm.nU;
+    int nv = 0;
+    uint32_t off = 0;
+    for (int it0 = first; it0 < last; it0 += 64) {
+      const int it = it0 + lane;
+      const bool live = it < last;
+      const uint32_t m = live ? sm.umask[it] : 0u;
+      const bool sh = it == nU;
+      const uint32_t vl = (uint32_t)((size_t)(sh ? p.Is : p.I) * ab / 16);
+      const int rows = __popc(m);
+      int pr = rows;
+      uint32_t pb = (uint32_t)rows * vl;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int tr = __shfl_up(pr, d);
+        const uint32_t tb = __shfl_up(pb, d);
+        if (lane >= d) {
+          pr += tr;
+          pb += tb;
+        }
+      }
+      if (live) {
+        int v = nv + pr - rows;
+        uint32_t o = off + pb - (uint32_t)rows * vl;
+        for (int r = 0; r < p.R; ++r)
+          if (m & (1u << r)) {
+            sm.voff[it][r] = (uint16_t)o;
+            sm.vsrc[v] = sh ? (uint32_t)(kHidShared | ((size_t)r * vl * 16))
+                            : (uint32_t)(((size_t)r * p.K + sm.uslot[it][r]) * vl * 16);
+            sm.vdst[v] = (uint16_t)o;
+            sm.vlen[v] = (uint16_t)vl;
+            ++v;
+            o += vl;
+          }
+      }
+      nv += __shfl(pr, 63);
+      off += __shfl(pb, 63);
+    }
+    if (lane == 0) sm.nv = nv;
+  }
+  __syncthreads();
+}
+
+/* Copies the listed hidden rows into LDS with coherent 16-byte loads: wave w takes rows
+ * w, w + 8, ...; each lane keeps up to 8 loads in flight before storing them. */
+__device__ __forceinline__ void stage_copy(const Params& p, Smem& sm, size_t ab) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t hr = coh_region(p.h_routed, (size_t)p.R * p.K * p.I * ab);
+  const __amdgpu_buffer_rsrc_t hsr = coh_region(p.h_shared, (size_t)p.R * (p.Is > 0 ? p.Is : 1) * ab);
+  const int nv = sm.nv;
+  int v = wave, ch = lane;
+  while (v < nv && ch >= (int)sm.vlen[v]) {
+    v += kWaves;
+    ch = lane;
+  }
+  constexpr int B = 8;
+  while (__ballot(v < nv) != 0ull) {
+    uint4 buf[B];
+    uint32_t dst[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      dst[b] = 0xFFFFFFFFu;
+      if (v < nv) {
+        const uint32_t src = sm.vsrc[v];
+        buf[b] = (src & kHidShared) ? coh_b128(hsr, (src & ~kHidShared) + ch * 16)
+                                    : coh_b128(hr, src + ch * 16);
+        dst[b] = (uint32_t)sm.vdst[v] + ch;
+        ch += 64;
+        while (v < nv && ch >= (int)sm.vlen[v]) {
+          v += kWaves;
+          ch = lane;
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+      if (dst[b] != 0xFFFFFFFFu) reinterpret_cast<uint4*>(sm.big)[dst[b]] = buf[b];
+  }
+  __syncthreads();
+}
+
 /* In the fused launch (FUSED), the wait for the gate/up barrier runs after this wave has issued
  * the loads of its first routed task (so they overlap the wait) and before any hidden row is
  * read. */
@@ -1270,7 +1615,8 @@ __device__ __forceinline__ bool ph_down(const Params& p, Smem& sm) {
   WRegs<RFMT, kRG, CHR> pre;
   WRegs<SFMT, kRG, Fmt<SFMT>::CH_DN> none;
   bool have_pre = false;
-  if (RMAX == 1 && wave < last * nq && wave / nq < nU) {
+  /* wave 0 polls the gate/up barrier: it issues no early loads that its polls would wait on */
+  if (RMAX == 1 && wave > 0 && wave < last * nq && wave / nq < nU) {
     const uint8_t* vr[kRG];
     const uint8_t* sr[kRG];
     down_rows<ACT, RFMT>(p, g, p.routed, sm.U[wave / nq], p.I, wave % nq, vr, sr);
@@ -1278,73 +1624,24 @@ __device__ __forceinline__ bool ph_down(const Params& p, Smem& sm) {
     have_pre = true;
   }
   if (FUSED) {
+    /* the expand's slice inputs and the staging list need nothing from the other workgroups:
+     * both are prepared while the last ones finish their gate/up rows */
+    const Slice c = slice_of(p);
+    SliceRegs sreg;
+    slice_prefetch<ACT>(p, c, sreg);
+    stage_list(p, sm, 0, last, ab);
     if (!bar_wait(p, sm, PH_GATEUP)) return false;
+    slice_store(p, c, sm, sreg);
     stamp(p, sm.trace_on != 0, 10);
   }
   int first = 0;
   while (first <= nU) {
     if (first > 0) last = down_group_end(p, sm, first, ab);
-    __syncthreads(); /* the previous group's tasks are done with the staging area */
-    if (tid == 0) {
-      size_t off = 0;
-      for (int it = first; it < last; ++it) {
-        const int inter = it == nU ? p.Is : p.I;
-        for (int r = 0; r < R; ++r)
-          if (sm.umask[it] & (1u << r)) {
-            sm.voff[it][r] = (uint16_t)(off / 16);
-            off += (size_t)inter * ab;
-          }
-      }
+    if (first > 0 || !FUSED) {
+      __syncthreads(); /* the previous group's tasks are done with the staging area */
+      stage_list(p, sm, first, last, ab);
     }
-    __syncthreads();
-    /* list the group's hidden rows, then copy them with batched coherent 16-byte loads */
-    if (tid == 0) {
-      int nv = 0;
-      for (int it = first; it < last; ++it)
-        for (int r = 0; r < R; ++r)
-          if (sm.umask[it] & (1u << r)) {
-            const size_t vbytes = (size_t)(it == nU ? p.Is : p.I) * ab;
-            sm.vsrc[nv] = it == nU ? (uint32_t)(kHidShared | (r * vbytes))
-                                   : (uint32_t)(((size_t)r * p.K + sm.uslot[it][r]) * vbytes);
-            sm.vdst[nv] = sm.voff[it][r];
-            sm.vlen[nv] = (uint16_t)(vbytes / 16);
-            ++nv;
-          }
-      sm.nv = nv;
-    }
-    __syncthreads();
-    {
-      const __amdgpu_buffer_rsrc_t hr =
-          coh_region(p.h_routed, (size_t)R * p.K * p.I * ab);
-      const __amdgpu_buffer_rsrc_t hsr =
-          coh_region(p.h_shared, (size_t)R * (p.Is > 0 ? p.Is : 1) * ab);
-      const int nv = sm.nv;
-      constexpr int B = 4;
-      for (int v0 = 0; v0 < nv; v0 += B) {
-        uint4 buf[B][2];
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int v = v0 + b, ch = tid + h * kBlock;
-            buf[b][h] = make_uint4(0, 0, 0, 0);
-            if (v < nv && ch < sm.vlen[v]) {
-              const uint32_t src = sm.vsrc[v];
-              buf[b][h] = (src & kHidShared) ? coh_b128(hsr, (src & ~kHidShared) + ch * 16)
-                                             : coh_b128(hr, src + ch * 16);
-            }
-          }
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int v = v0 + b, ch = tid + h * kBlock;
-            if (v < nv && ch < sm.vlen[v])
-              *reinterpret_cast<uint4*>(sm.big + (size_t)sm.vdst[v] * 16 + (size_t)ch * 16) = buf[b][h];
-          }
-      }
-    }
-    __syncthreads();
+    stage_copy(p, sm, ab);
     if (FUSED && first == 0) stamp(p, sm.trace_on != 0, 21);
     const int ntask = (last - first) * nq;
     for (int t = wave; t < ntask; t += kWaves) {
@@ -1382,15 +1679,63 @@ __device__ __forceinline__ bool ph_down(const Params& p, Smem& sm) {
  * Phase: expand + carry for the workgroup's slice [ds4 HC fusion commit: post/comb expand +
  * BF16; SGLang fused post/pre page: bf16 residual materialisation + next pre-norm GEMM
  * partials + RMS square-sum partials]. new[i][h] = bf16(post_i block[h] + sum_j comb[i][j]
- * state_j[h]). The carry is taken on the rounded new state; per-workgroup partials are summed
- * in workgroup order by the last workgroup to finish. */
+ * state_j[h]). The carry is taken on the rounded new state: every workgroup writes its 25 R
+ * partial sums, each tagged with the launch epoch; output q of the carry is then summed over
+ * the workgroups in a fixed order (reduce_carry). */
+/* Carry output q (row q / 25, output q % 25) = sum over the grid's tagged partials, in the
+ * order: lane L adds workgroups L, L + 64, ... in turn, then a wave sum. With check, waits
+ * (bounded) until every partial carries `tag`. Whole workgroup; returns false on expiry. */
+__device__ __forceinline__ bool reduce_carry(const Params& p, Smem& sm, int q, bool check,
+                                             uint32_t tag) {
+  const int tid = threadIdx.x, G = gridDim.x;
+  const __amdgpu_buffer_rsrc_t cp =
+      coh_region(p.carry_part, (size_t)p.R * kNCarry * G * 8);
+  int ok = 1;
+  for (int w = tid; w < G; w += kBlock) {
+    const uint32_t off = (uint32_t)(((size_t)q * G + w) * 8);
+    uint2 v = coh_b64(cp, off);
+    if (check && v.y != tag) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (v.y != tag) {
+        __builtin_amdgcn_s_sleep(2);
+        v = coh_b64(cp, off);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > sm.spin) {
+          ok = 0;
+          break;
+        }
+      }
+    }
+    sm.cred[w] = __uint_as_float(v.x);
+  }
+  const bool all = __syncthreads_and(ok) != 0;
+  if (!all && tid == 0) report_timeout(p, PH_END);
+  if (tid < 64) {
+    float t = 0.0f;
+    for (int w = tid; w < G; w += 64) t += sm.cred[w];
+    t = wave_sum(t);
+    if (tid == 0 && all) {
+      p.carry_out[q] = t;
+      if (p.carry_ws) p.carry_ws[q] = t;
+    }
+  }
+  __syncthreads();
+  return all;
+}
+
+/* End-of-launch arrival (no data is published by it): advances this workgroup's end counter
+ * once per fused launch, which the next launch reads as its epoch. */
+__device__ __forceinline__ void end_arrive(const Params& p) {
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(bar_counter(p, PH_END, blockIdx.x % kBarGroups), (uint64_t)1,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int ACT, int RMAX, bool FUSED>
 __device__ __forceinline__ void ph_expand(const Params& p, Smem& sm, const float* blk) {
   const int tid = threadIdx.x;
-  const int hs = (p.H + p.nslice - 1) / p.nslice;
-  const int h0 = blockIdx.x * hs;
-  int nh = p.H - h0 < hs ? p.H - h0 : hs;
-  if (nh < 0) nh = 0;
+  const Slice c = slice_of(p);
+  const int h0 = c.h0, nh = c.nh;
   const int R = p.R, H = p.H, n = 4 * H;
   /* new state: one thread per hidden position reads all 4 streams and writes all 4, so the
    * output may alias the input */
@@ -1399,18 +1744,20 @@ __device__ __forceinline__ void ph_expand(const Params& p, Smem& sm, const float
     const int h = h0 + hl;
     for (int r = 0; r < R; ++r) {
       const size_t sb = (size_t)r * n + h;
-      const float s0 = act_ld<ACT>(p.state, sb), s1 = act_ld<ACT>(p.state, sb + H);
-      const float s2 = act_ld<ACT>(p.state, sb + 2 * (size_t)H);
-      const float s3 = act_ld<ACT>(p.state, sb + 3 * (size_t)H);
+      float sv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sv[i] = c.lds ? sm.sslice[(r * 4 + i) * kSliceMax + hl]
+                      : act_ld<ACT>(p.state, sb + (size_t)i * H);
       const float b = blk[hl * R + r];
       float nv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float a = sm.post[r][i] * b;
-        a = fmaf(sm.comb[r][4 * i + 0], s0, a);
-        a = fmaf(sm.comb[r][4 * i + 1], s1, a);
-        a = fmaf(sm.comb[r][4 * i + 2], s2, a);
-        a = fmaf(sm.comb[r][4 * i + 3], s3, a);
+        a = fmaf(sm.comb[r][4 * i + 0], sv[0], a);
+        a = fmaf(sm.comb[r][4 * i + 1], sv[1], a);
+        a = fmaf(sm.comb[r][4 * i + 2], sv[2], a);
+        a = fmaf(sm.comb[r][4 * i + 3], sv[3], a);
         nv[i] = act_round<ACT>(a);
       }
 #pragma unroll
@@ -1421,20 +1768,22 @@ __device__ __forceinline__ void ph_expand(const Params& p, Smem& sm, const float
     }
   }
   if (p.w_mix_next == nullptr) {
-    if (FUSED) arrive_last(p, sm); /* keeps every end counter advancing once per launch */
+    if (FUSED) end_arrive(p);
     return;
   }
   stamp(p, sm.trace_on != 0, 12);
   __syncthreads();
   /* carry partials of this slice: cp[j][r][hl] = sum_i W_next[j][i H + h] new[r][i] (j < 24),
    * cp[24][r][hl] = sum_i new[r][i]^2; then summed over hl in order */
-  float* cp = nvb + (size_t)nh * R * 4; /* [25][R][nh] */
+  float* cpl = nvb + (size_t)nh * R * 4; /* [25][R][nh] */
   for (int q = tid; q < nh * kNCarry; q += kBlock) {
     const int hl = q % nh, j = q / nh, h = h0 + hl;
     float w[4];
     if (j < kNMix) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = p.w_mix_next[(size_t)j * n + (size_t)i * H + h];
+      for (int i = 0; i < 4; ++i)
+        w[i] = c.lds ? sm.wnext[(j * 4 + i) * kSliceMax + hl]
+                     : p.w_mix_next[(size_t)j * n + (size_t)i * H + h];
     }
     for (int r = 0; r < R; ++r) {
       const float* v = nvb + (hl * R + r) * 4;
@@ -1450,32 +1799,26 @@ __device__ __forceinline__ void ph_expand(const Params& p, Smem& sm, const float
         a = fmaf(v[2], v[2], a);
         a = fmaf(v[3], v[3], a);
       }
-      cp[((size_t)j * R + r) * nh + hl] = a;
+      cpl[((size_t)j * R + r) * nh + hl] = a;
     }
   }
   __syncthreads();
+  const uint32_t tag = FUSED ? (uint32_t)(sm.epoch + 1) : 0u;
   if (tid < R * kNCarry) {
     const int j = tid % kNCarry, r = tid / kNCarry;
-    const float* c = cp + ((size_t)j * R + r) * nh;
+    const float* cl = cpl + ((size_t)j * R + r) * nh;
     float t = 0.0f;
-    for (int hl = 0; hl < nh; ++hl) t += c[hl];
-    stf_coh(p.carry_part + (size_t)blockIdx.x * R * kNCarry + tid, t);
+    for (int hl = 0; hl < nh; ++hl) t += cl[hl];
+    /* partial (q = tid, workgroup) at [q][grid]: value in the low word, tag in the high word */
+    st_coh(reinterpret_cast<uint64_t*>(p.carry_part) + (size_t)tid * gridDim.x + blockIdx.x,
+           ((uint64_t)tag << 32) | __float_as_uint(t));
   }
-  /* the last workgroup to finish sums the partials in workgroup order */
-  if (FUSED ? arrive_last(p, sm) : arrive_last_single(p, sm)) {
-    /* every wave takes (row, output) pairs; lanes take workgroups w = lane + 64 m */
-    const int lane = tid & 63, wave = tid >> 6;
-    const __amdgpu_buffer_rsrc_t cpr = coh_region(p.carry_part, (size_t)gridDim.x * R * kNCarry * 4);
-    for (int q = wave; q < R * kNCarry; q += kWaves) {
-      float t = 0.0f;
-      for (int w = lane; w < (int)gridDim.x; w += 64)
-        t += coh_f32(cpr, (uint32_t)(((size_t)w * R * kNCarry + q) * 4));
-      t = wave_sum(t);
-      if (lane == 0) {
-        p.carry_out[q] = t;
-        if (p.carry_ws) p.carry_ws[q] = t;
-      }
-    }
+  if (FUSED) {
+    end_arrive(p);
+    for (int q = blockIdx.x; q < R * kNCarry; q += gridDim.x)
+      if (!reduce_carry(p, sm, q, true, tag)) return;
+  } else if (arrive_last_single(p, sm)) {
+    for (int q = 0; q < R * kNCarry; ++q) reduce_carry(p, sm, q, false, 0u);
   }
 }
 
@@ -1499,9 +1842,10 @@ __global__ void __launch_bounds__(kBlock) k_hc_pre(Params p) {
 template <int ACT, int RMAX>
 __global__ void __launch_bounds__(kBlock) k_router_logits(Params p) {
   __shared__ Smem sm;
+  if (threadIdx.x == 0) sm.trace_on = 0;
   load_act_rows<ACT>(p.norm_in, p.R, p.H, sm);
   RouterRegs none;
-  ph_router<ACT, RMAX, false>(p, sm, none);
+  ph_router<ACT, RMAX, false>(p, sm, none, 0u, false);
 }
 
 template <int UNUSED>
@@ -1510,12 +1854,13 @@ __global__ void __launch_bounds__(kBlock) k_select(Params p) {
   if (threadIdx.x == 0) sm.trace_on = 0;
   load_bias(p, sm);
   __syncthreads();
-  ph_select(p, sm, true);
+  ph_select(p, sm, true, false, 0u);
 }
 
 template <int ACT, int RFMT, int SFMT, int RMAX>
 __global__ void __launch_bounds__(kBlock) k_gateup(Params p) {
   __shared__ Smem sm;
+  if (threadIdx.x == 0) sm.trace_on = 0;
   load_act_rows<ACT>(p.norm_in, p.R, p.H, sm);
   load_selection(p, sm);
   ph_plan(p, sm);
@@ -1535,6 +1880,7 @@ __global__ void __launch_bounds__(kBlock) k_down(Params p) {
 template <int ACT, int RMAX>
 __global__ void __launch_bounds__(kBlock) k_expand(Params p) {
   __shared__ Smem sm;
+  if (threadIdx.x == 0) sm.trace_on = 0;
   const int tid = threadIdx.x;
   if (tid < p.R * 4) sm.post[tid / 4][tid % 4] = p.post_in[tid];
   if (tid < p.R * 16) sm.comb[tid / 16][tid % 16] = p.comb_in[tid];
@@ -1542,6 +1888,12 @@ __global__ void __launch_bounds__(kBlock) k_expand(Params p) {
   int nh = p.H - h0 < hs ? p.H - h0 : hs;
   if (nh < 0) nh = 0;
   float* blk = reinterpret_cast<float*>(sm.big + kLdsHidBytes);
+  {
+    const Slice c = slice_of(p);
+    SliceRegs sreg;
+    slice_prefetch<ACT>(p, c, sreg);
+    slice_store(p, c, sm, sreg);
+  }
   for (int q = tid; q < nh * p.R; q += kBlock) {
     const int hl = q / p.R, r = q % p.R;
     blk[q] = act_ld<ACT>(p.block_in, (size_t)r * p.H + h0 + hl);
@@ -1553,8 +1905,10 @@ __global__ void __launch_bounds__(kBlock) k_expand(Params p) {
 /* The whole layer half in one persistent launch (one workgroup per compute unit):
  *   mix partials | arrive 1, load the pre-side parameters, wait 1 | pre side (every workgroup)
  *   | router rows | arrive 2, shared-expert gate/up, wait 2 | select + plan (every workgroup)
- *   | routed gate/up | arrive 3, issue the first down-projection loads, wait 3 | down, block
- *   | expand + carry (the last workgroup to finish sums the carry).
+ *   | routed gate/up | arrive 3, issue the first down-projection loads and the expand's slice
+ *   inputs, list the hidden rows to stage, wait 3 | down, block | expand + carry partials
+ *   (workgroup q then sums carry output q over the grid once every partial carries this
+ *   launch's tag).
  * Trace slots: 0 start, 1 mix partials, 2 pre-side inputs ready, 3 pre side, 4 router,
  * 5 shared gate/up, 6 router barrier passed, 7 select, 8 plan, 9 routed gate/up,
  * 10 gate/up barrier passed, 11 down + block, 12 expand, 13 carry. */
@@ -1582,16 +1936,23 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
     __syncthreads();
   }
   stamp(p, tr, 2);
-  ph_hc_pre<ACT, RMAX>(p, sm, blockIdx.x == 0);
+  if (threadIdx.x == 0) {
+    sm.sel_ok = 1;
+    sm.shared_next = 0;
+  }
+  ph_hc_pre<ACT, RMAX>(p, sm, blockIdx.x == 0); /* its barriers publish the two words above */
   stamp(p, tr, 3);
-  ph_router<ACT, RMAX, true>(p, sm, rpre);
+  const uint32_t tag = (uint32_t)(sm.epoch + 1);
+  /* router parts (waves 1 ..), then the select (waves 0 .. R - 1, polling the tagged logits),
+   * then the shared expert's gate/up rows, claimed by whichever waves are free */
+  ph_router<ACT, RMAX, true>(p, sm, rpre, tag, sm.skip_phase == PH_ROUTER);
   stamp(p, tr, 4);
-  bar_arrive(p, sm, PH_ROUTER);
-  ph_gateup_shared<ACT, SFMT, RMAX>(p, sm);
-  stamp(p, tr, 5);
-  if (!bar_wait(p, sm, PH_ROUTER)) return;
+  select_rows(p, sm, blockIdx.x == 0, true, tag);
   stamp(p, tr, 6);
-  ph_select(p, sm, blockIdx.x == 0);
+  ph_gateup_shared_claim<ACT, SFMT, RMAX>(p, sm);
+  stamp(p, tr, 5);
+  __syncthreads();
+  if (!select_finish(p, sm, blockIdx.x == 0)) return;
   stamp(p, tr, 7);
   ph_plan(p, sm);
   stamp(p, tr, 8);

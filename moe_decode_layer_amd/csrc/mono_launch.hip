@@ -52,9 +52,15 @@ static int launch_act(Kernel k, const Params& p, int rfmt, int sfmt, int grid, h
   }
 }
 
-__global__ void k_ws_init(uint32_t* ctl) {
+/* Control words to their initial values, and the tagged regions (carry partials, router logit
+ * parts) to tag 0, which no fused launch writes, so that values left by launches before the
+ * init are never taken as current. */
+__global__ void k_ws_init(uint32_t* ctl, uint64_t* tagged, size_t tag_words) {
   const int t = threadIdx.x;
-  if (t < CTL_WORDS) ctl[t] = (t == CTL_FAULT_WG) ? 0xFFFFFFFFu : 0u;
+  if (blockIdx.x == 0 && t < CTL_WORDS) ctl[t] = (t == CTL_FAULT_WG) ? 0xFFFFFFFFu : 0u;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + t; i < tag_words;
+       i += (size_t)gridDim.x * blockDim.x)
+    tagged[i] = 0u;
 }
 
 __global__ void k_ws_debug(uint32_t* ctl, uint32_t spin, uint32_t fwg, uint32_t fph) {
@@ -72,7 +78,8 @@ __global__ void k_ws_trace(uint32_t* ctl, uint32_t on) {
 int launch(Kernel k, const Params& p, int act, int rfmt, int sfmt, int grid, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (k == K_WS_INIT) {
-    hipLaunchKernelGGL(k_ws_init, dim3(1), dim3(CTL_WORDS), 0, st, p.ctl);
+    hipLaunchKernelGGL(k_ws_init, dim3(64), dim3(256), 0, st, p.ctl,
+                       reinterpret_cast<uint64_t*>(p.carry_part), p.tag_words);
     return (int)hipGetLastError();
   }
   const bool one = p.R <= 1;

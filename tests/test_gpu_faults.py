@@ -1,7 +1,8 @@
-"""Failure handling of the persistent launch, forced from the host: one workgroup skips its
-arrival at a grid barrier and the wait limit is shortened, so every waiting workgroup's bounded
-wait expires, the error word is set and the launch ends normally (no hang, no fault). After
-mono_workspace_init the workspace works again and gives the same bytes as a fresh one."""
+"""Failure handling of the persistent launch, forced from the host: workgroup 0 skips its
+arrival at a grid barrier (or, for the router, the store of its tagged logit parts) and the wait
+limit is shortened, so every waiting workgroup's bounded wait expires, the error word is set and
+the launch ends normally (no hang, no fault). After mono_workspace_init the workspace works
+again and gives the same bytes as a fresh one."""
 
 import numpy as np
 import pytest
@@ -25,15 +26,15 @@ def test_skipped_arrival_times_out_and_recovers(phase):
     wn = g.layers[1]["w_mix"]
     ref = g.fused(st, 0, None, wn)
     grid = mono.mono_grid_size()
-    # 2 ms limit (100 MHz counter); workgroup grid - 1 never arrives at `phase`
-    mono.mono_workspace_set_debug(g.ws, 200000, grid - 1, phase, support.stream())
+    # 2 ms limit (100 MHz counter); workgroup 0 never arrives at `phase` (it has router work)
+    mono.mono_workspace_set_debug(g.ws, 200000, 0, phase, support.stream())
     new = g.buf(SMALL.rows * 4 * SMALL.hidden * 2)
     carry = g.buf(SMALL.rows * 25 * 4)
     mono.mono_ffn_layer(g.shape, g.structs[0], wn, st, None, new, carry, g.ws, support.stream())
     status, err = mono.mono_workspace_poll(g.ws, support.stream())
     assert status == mono.MONO_E_TIMEOUT
     assert err[0] == 1 and err[1] == phase and 0 <= err[2] < grid
-    assert err[3] == grid   # every workgroup waited at that barrier and gave up once
+    assert err[3] == grid   # every workgroup waited there and gave up once
     mono.mono_workspace_init(g.ws, g.shape, support.stream())
     again = g.fused(st, 0, None, wn)
     support.assert_same(again, ref, ["mixes", "logits", "idx", "weights", "h_routed", "block",
