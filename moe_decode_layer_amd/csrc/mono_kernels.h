@@ -409,7 +409,8 @@ struct Smem {
   uint32_t umask[kMaxUnion + 1];
   int8_t uslot[kMaxUnion + 1][kMaxRows];
   uint16_t voff[kMaxUnion + 1][kMaxRows]; /* staged hidden row offset per (item, row), 16 B */
-  uint8_t used[kMaxExperts];
+  uint32_t ubits[kMaxExperts / 32]; /* plan: selected experts as a bitmap */
+  int ubase[kMaxExperts / 32];       /* plan: distinct experts before each bitmap word */
   uint32_t vsrc[kMaxStaged]; /* staged hidden rows: source offset (flag: shared), */
   uint16_t vdst[kMaxStaged]; /* LDS offset in 16 B, */
   uint16_t vlen[kMaxStaged]; /* length in 16 B */
@@ -672,33 +673,6 @@ __device__ __forceinline__ void ph_hc_pre(const Params& p, Smem& sm, bool write_
       if (write_out) p.post[r * 4 + i] = v;
     }
   }
-  /* Sinkhorn: 16 lanes per row hold M[i][j] at lane 16 (r % 4) + 4 i + j; row sums with quad
-   * butterflies, column sums with two rotations inside the 16-lane row (each lane associates
-   * its column sum in its own fixed order); each normalisation multiplies by the hardware
-   * reciprocal of the sum */
-  if (wave < (R + 3) / 4) {
-    const int r = wave * 4 + (lane >> 4), q = lane & 15;
-    const bool live = r < R;
-    const float* m = sm.mixes[live ? r : 0];
-    const float L = sm.hcs[2] * m[8 + q] + sm.hcb[8 + q];
-    float mx = fmaxf(L, dpp<0xB1>(L));
-    mx = fmaxf(mx, dpp<0x4E>(mx));
-    mx = fmaxf(mx, dpp<0x124>(mx)); /* row_ror:4 */
-    mx = fmaxf(mx, dpp<0x128>(mx)); /* row_ror:8 */
-    float M = expf(L - mx);
-    for (int it = 0; it < p.iters; ++it) {
-      float rs = M + dpp<0xB1>(M);
-      rs = rs + dpp<0x4E>(rs);
-      M = M * __builtin_amdgcn_rcpf(rs);
-      float cs = M + dpp<0x124>(M);
-      cs = cs + dpp<0x128>(cs);
-      M = M * __builtin_amdgcn_rcpf(cs);
-    }
-    if (live) {
-      sm.comb[r][q] = M;
-      if (write_out) p.comb[r * 16 + q] = M;
-    }
-  }
   __syncthreads();
   stamp(p, sm.trace_on != 0, 16);
   /* collapse: x = bf16(sum_i pre_i state_i), VE consecutive positions per thread, 16-byte
@@ -822,6 +796,40 @@ __device__ __forceinline__ void ph_hc_pre(const Params& p, Smem& sm, bool write_
     }
   }
   __syncthreads();
+}
+
+/* comb = Sinkhorn(exp(a2 m[8 + 4 i + j] + b[8 + 4 i + j] - max)) for every row, run by waves
+ * 0 .. (R + 3) / 4 - 1 with no workgroup barrier (comb is first read by the expand). Needs the
+ * mixes in LDS. */
+__device__ __forceinline__ void ph_sinkhorn(const Params& p, Smem& sm, bool write_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, R = p.R;
+  /* Sinkhorn: 16 lanes per row hold M[i][j] at lane 16 (r % 4) + 4 i + j; row sums with quad
+   * butterflies, column sums with two rotations inside the 16-lane row (each lane associates
+   * its column sum in its own fixed order); each normalisation multiplies by the hardware
+   * reciprocal of the sum */
+  if (wave < (R + 3) / 4) {
+    const int r = wave * 4 + (lane >> 4), q = lane & 15;
+    const bool live = r < R;
+    const float* m = sm.mixes[live ? r : 0];
+    const float L = sm.hcs[2] * m[8 + q] + sm.hcb[8 + q];
+    float mx = fmaxf(L, dpp<0xB1>(L));
+    mx = fmaxf(mx, dpp<0x4E>(mx));
+    mx = fmaxf(mx, dpp<0x124>(mx)); /* row_ror:4 */
+    mx = fmaxf(mx, dpp<0x128>(mx)); /* row_ror:8 */
+    float M = expf(L - mx);
+    for (int it = 0; it < p.iters; ++it) {
+      float rs = M + dpp<0xB1>(M);
+      rs = rs + dpp<0x4E>(rs);
+      M = M * __builtin_amdgcn_rcpf(rs);
+      float cs = M + dpp<0x124>(M);
+      cs = cs + dpp<0x128>(cs);
+      M = M * __builtin_amdgcn_rcpf(cs);
+    }
+    if (live) {
+      sm.comb[r][q] = M;
+      if (write_out) p.comb[r * 16 + q] = M;
+    }
+  }
 }
 
 /* Copies R act rows [R][H] from global memory into sm.big. */
@@ -1238,45 +1246,49 @@ __device__ __forceinline__ void load_selection(const Params& p, Smem& sm) {
 
 /* Plan: the distinct selected experts in ascending order (each is streamed once for all the
  * rows that chose it), with the rows that use it and the slot j it fills in each row. Item nU
- * is the shared expert (every row). */
+ * is the shared expert (every row). Built by wave 0 alone from a bitmap of the selected
+ * experts (LDS operations of one wave complete in order); every wave sees it after the
+ * __syncthreads at the end. */
 __device__ __forceinline__ void ph_plan(const Params& p, Smem& sm) {
-  const int tid = threadIdx.x, R = p.R, K = p.K, E = p.E;
-  for (int e = tid; e < E; e += kBlock) sm.used[e] = 0;
-  __syncthreads();
-  if (tid < R * K) sm.used[sm.sel_e[tid / K][tid % K]] = 1;
-  __syncthreads();
-  if (tid < 64) {
-    int base = 0;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-      const int e = e0 + tid;
-      const bool u = e < E && sm.used[e];
-      const uint64_t bal = __ballot(u);
-      if (u) sm.U[base + __popcll(bal & ((1ull << tid) - 1ull))] = e;
-      base += __popcll(bal);
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x, R = p.R, K = p.K, RK = p.R * p.K;
+    constexpr int NW = kMaxExperts / 32;
+    if (lane < NW) sm.ubits[lane] = 0u;
+    for (int q = lane; q < RK; q += 64) {
+      const int e = sm.sel_e[q / K][q % K];
+      atomicOr(&sm.ubits[e >> 5], 1u << (e & 31));
     }
-    if (tid == 0) sm.nU = base;
-  }
-  __syncthreads();
-  const int nU = sm.nU;
-  for (int q = tid; q < (nU + 1) * kMaxRows; q += kBlock) {
-    const int u = q / kMaxRows, r = q % kMaxRows;
-    int slot = -1;
-    if (r < R) {
-      if (u == nU) {
-        slot = K;
-      } else {
-        for (int j = 0; j < K; ++j)
-          if (sm.sel_e[r][j] == sm.U[u]) slot = j;
+    uint32_t w = lane < NW ? sm.ubits[lane] : 0u;
+    const int c = __popc(w);
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < NW; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    const int base = incl - c;
+    const int nU = __shfl(incl, NW - 1);
+    if (lane < NW) {
+      sm.ubase[lane] = base;
+      int k = base;
+      while (w) {
+        sm.U[k++] = lane * 32 + (__ffs(w) - 1);
+        w &= w - 1u;
       }
     }
-    sm.uslot[u][r] = (int8_t)slot;
-  }
-  __syncthreads();
-  if (tid <= nU) {
-    uint32_t m = 0;
-    for (int r = 0; r < R; ++r)
-      if (sm.uslot[tid][r] >= 0) m |= 1u << r;
-    sm.umask[tid] = m;
+    for (int q = lane; q < (nU + 1) * kMaxRows; q += 64) sm.uslot[q / kMaxRows][q % kMaxRows] = -1;
+    for (int u = lane; u <= nU; u += 64) sm.umask[u] = 0u;
+    for (int q = lane; q < RK; q += 64) {
+      const int r = q / K, j = q % K, e = sm.sel_e[r][j];
+      const int u = sm.ubase[e >> 5] + __popc(sm.ubits[e >> 5] & ((1u << (e & 31)) - 1u));
+      sm.uslot[u][r] = (int8_t)j;
+      atomicOr(&sm.umask[u], 1u << r);
+    }
+    for (int r = lane; r < R; r += 64) sm.uslot[nU][r] = (int8_t)K;
+    if (lane == 0) {
+      sm.umask[nU] = (1u << R) - 1u;
+      sm.nU = nU;
+    }
   }
   __syncthreads();
 }
@@ -1837,6 +1849,7 @@ __global__ void __launch_bounds__(kBlock) k_hc_pre(Params p) {
   load_pre_params<ACT>(p, sm);
   __syncthreads();
   ph_hc_pre<ACT, RMAX>(p, sm, true);
+  ph_sinkhorn(p, sm, true);
 }
 
 template <int ACT, int RMAX>
@@ -1947,6 +1960,7 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
    * then the shared expert's gate/up rows, claimed by whichever waves are free */
   ph_router<ACT, RMAX, true>(p, sm, rpre, tag, sm.skip_phase == PH_ROUTER);
   stamp(p, tr, 4);
+  ph_sinkhorn(p, sm, blockIdx.x == 0); /* comb is needed only by the expand */
   select_rows(p, sm, blockIdx.x == 0, true, tag);
   stamp(p, tr, 6);
   ph_gateup_shared_claim<ACT, SFMT, RMAX>(p, sm);
