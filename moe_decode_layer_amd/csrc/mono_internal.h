@@ -142,7 +142,7 @@ inline WsLayout ws_layout(const mono_shape& s) {
   L.mix_part = take(nchunk * R * kNCarry * 4);
   L.carry_part = take((size_t)kMaxGrid * R * kNCarry * 8);
   L.lgp = take(router_parts(s.hidden) * R * E * 8);
-  L.lgp_end = o;
+  L.lgp_end = o; /* the workspace init clears [carry_part, lgp_end) */
   L.mixes = take(R * kNMix * 4);
   L.pre = take(R * 4 * 4);
   L.post = take(R * 4 * 4);

@@ -1357,13 +1357,13 @@ __device__ __forceinline__ void ph_gateup_shared_claim(const Params& p, Smem& sm
   }
 }
 
-/* Routed gate/up: the nU * I tasks split into equal contiguous ranges, one per wave. */
+/* Routed gate/up: task t of the nU * I tasks goes to wave t % waves of the grid, spread over
+ * compute units first, so that at any moment the grid streams one contiguous stretch of rows. */
 template <int ACT, int RFMT, int RMAX>
 __device__ __forceinline__ void ph_gateup_routed(const Params& p, const Smem& sm) {
   const long T = (long)sm.nU * p.I;
-  const long gw = (long)blockIdx.x * kWaves + (threadIdx.x >> 6), nwt = (long)gridDim.x * kWaves;
-  const long t0 = T * gw / nwt, t1 = T * (gw + 1) / nwt;
-  for (long t = t0; t < t1; ++t) {
+  const long nwt = (long)gridDim.x * kWaves;
+  for (long t = wave_major_id(); t < T; t += nwt) {
     const int u = (int)(t / p.I), i = (int)(t % p.I);
     gateup_task<ACT, RFMT, RMAX>(p, sm, p.routed, sm.U[u], i, p.I, sm.umask[u], u, false);
   }
