@@ -121,8 +121,10 @@ typedef struct {
 /* Bytes of workspace a step of this shape needs (0 if the shape is invalid). */
 size_t mono_workspace_bytes(const mono_shape* shape);
 
-/* Enqueues the initialisation of ws (counters, error word, debug fields). Needed once before
- * first use and after a MONO_E_TIMEOUT. */
+/* Enqueues the initialisation of ws (counters, error word, debug fields, tagged regions). Needed
+ * once before first use, after a MONO_E_TIMEOUT, and when the workspace is used for a different
+ * shape (the fused launch tags the values it exchanges between workgroups with a launch count;
+ * the init clears the tags). */
 mono_status mono_workspace_init(void* ws, const mono_shape* shape, void* stream);
 
 /* Synchronises `stream`, then copies the workspace error word to err[4] (host memory):
@@ -157,8 +159,10 @@ typedef enum {
   MONO_T_LOGITS = 6,   /* [R][E] f32 */
   MONO_T_IDX = 7,      /* [R][k] int32 */
   MONO_T_WEIGHTS = 8,  /* [R][k] f32 */
-  MONO_T_H_ROUTED = 9, /* [R][k][I] act: SwiGLU hidden rows of the selected experts */
-  MONO_T_H_SHARED = 10,/* [R][Is] act */
+  MONO_T_H_ROUTED = 9, /* [R][k][I] SwiGLU hidden rows of the selected experts, each value tagged:
+                          bf16 act: uint32 = bf16 bits | tag << 16; f32 act: uint64 = f32 bits |
+                          tag << 32 (the tag orders the fused launch's workgroups) */
+  MONO_T_H_SHARED = 10,/* [R][Is], tagged as MONO_T_H_ROUTED */
   MONO_T_SHARED = 11,  /* [R][H] act */
   MONO_T_ROUTED = 12,  /* [R][H] f32 */
   MONO_T_BLOCK = 13,   /* [R][H] act */

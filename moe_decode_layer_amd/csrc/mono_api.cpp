@@ -309,8 +309,8 @@ mono_status mono_workspace_tensor(const mono_shape* shape, void* ws, mono_tensor
     case MONO_T_LOGITS: off = W.logits; n = R * shape->n_experts * 4; break;
     case MONO_T_IDX: off = W.idx; n = R * shape->top_k * 4; break;
     case MONO_T_WEIGHTS: off = W.weights; n = R * shape->top_k * 4; break;
-    case MONO_T_H_ROUTED: off = W.h_routed; n = R * shape->top_k * shape->inter * ab; break;
-    case MONO_T_H_SHARED: off = W.h_shared; n = R * shape->shared_inter * ab; break;
+    case MONO_T_H_ROUTED: off = W.h_routed; n = R * shape->top_k * shape->inter * ab * 2; break;
+    case MONO_T_H_SHARED: off = W.h_shared; n = R * shape->shared_inter * ab * 2; break;
     case MONO_T_SHARED: off = W.shared; n = R * H * ab; break;
     case MONO_T_ROUTED: off = W.routed; n = R * H * 4; break;
     case MONO_T_BLOCK: off = W.block; n = R * H * ab; break;

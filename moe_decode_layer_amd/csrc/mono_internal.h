@@ -87,8 +87,8 @@ struct Params {
   float* logits;
   int32_t* idx;
   float* weights;
-  void* h_routed;
-  void* h_shared;
+  void* h_routed;    /* [R][K][I] tagged hidden rows of the selected experts */
+  void* h_shared;    /* [R][Is] tagged hidden rows of the shared expert */
   void* shared_out;
   float* routed_out;
   void* block;
@@ -142,6 +142,10 @@ inline WsLayout ws_layout(const mono_shape& s) {
   L.mix_part = take(nchunk * R * kNCarry * 4);
   L.carry_part = take((size_t)kMaxGrid * R * kNCarry * 8);
   L.lgp = take(router_parts(s.hidden) * R * E * 8);
+  /* hidden rows, tagged: each value with the launch tag beside it (bf16 | tag16 << 16 in a
+   * uint32, or f32 | tag32 << 32 in a uint64) */
+  L.h_routed = take(R * k * I * ab * 2);
+  L.h_shared = take(R * (Is > 0 ? Is : 1) * ab * 2);
   L.lgp_end = o; /* the workspace init clears [carry_part, lgp_end) */
   L.mixes = take(R * kNMix * 4);
   L.pre = take(R * 4 * 4);
@@ -152,8 +156,6 @@ inline WsLayout ws_layout(const mono_shape& s) {
   L.logits = take(R * E * 4);
   L.idx = take(R * k * 4);
   L.weights = take(R * k * 4);
-  L.h_routed = take(R * k * I * ab);
-  L.h_shared = take(R * (Is > 0 ? Is : 1) * ab);
   L.shared = take(R * H * ab);
   L.routed = take(R * H * 4);
   L.block = take(R * H * ab);

@@ -127,6 +127,15 @@ __device__ __forceinline__ void act_st_coh(void* p, size_t i, float v) {
     st_coh(static_cast<uint16_t*>(p) + i, (uint16_t)f2bf(v));
 }
 
+/* Tagged hidden-row value: bf16 bits | tag << 16 (uint32) or f32 bits | tag << 32 (uint64). */
+template <int ACT>
+__device__ __forceinline__ void hid_store(void* base, size_t i, float v, uint32_t tag) {
+  if (ACT == F32)
+    st_coh(static_cast<uint64_t*>(base) + i, ((uint64_t)tag << 32) | __float_as_uint(v));
+  else
+    st_coh(static_cast<uint32_t*>(base) + i, (tag << 16) | f2bf(v));
+}
+
 /* Device-coherent (sc1) loads issued as buffer loads: unlike atomic loads they are ordinary
  * memory operations, so a wave keeps many in flight. Offsets are bytes inside the region the
  * resource covers; reads past its end return 0. */
@@ -1301,7 +1310,7 @@ __device__ __forceinline__ void ph_plan(const Params& p, Smem& sm) {
 template <int ACT, int FMT, int RMAX>
 __device__ __forceinline__ void gateup_task(const Params& p, const Smem& sm, const Mat& m,
                                             int e, int i, int inter, uint32_t mask, int u,
-                                            bool is_shared) {
+                                            bool is_shared, uint32_t htag, bool hskip) {
   const int H = p.H, lane = threadIdx.x & 63;
   const size_t vb = row_vbytes(FMT, H), sb = row_sbytes(FMT, H);
   const size_t row = (size_t)e * inter + i;
@@ -1320,11 +1329,11 @@ __device__ __forceinline__ void gateup_task(const Params& p, const Smem& sm, con
     const float g = act_round<ACT>(wave_sum(acc[0][r]));
     const float uu = act_round<ACT>(wave_sum(acc[1][r]));
     const float h = act_round<ACT>(g / (1.0f + expf(-g)) * uu);
-    if (lane == 0) {
+    if (lane == 0 && !hskip) {
       if (is_shared)
-        act_st_coh<ACT>(p.h_shared, (size_t)r * p.Is + i, h);
+        hid_store<ACT>(p.h_shared, (size_t)r * p.Is + i, h, htag);
       else
-        act_st_coh<ACT>(p.h_routed, ((size_t)r * p.K + sm.uslot[u][r]) * p.I + i, h);
+        hid_store<ACT>(p.h_routed, ((size_t)r * p.K + sm.uslot[u][r]) * p.I + i, h, htag);
     }
   }
 }
@@ -1336,14 +1345,15 @@ __device__ __forceinline__ void ph_gateup_shared(const Params& p, const Smem& sm
   const int nwt = gridDim.x * kWaves;
   const uint32_t mask = (1u << p.R) - 1u;
   for (int i = wave_major_id(); i < p.Is; i += nwt)
-    gateup_task<ACT, SFMT, RMAX>(p, sm, p.shared, 0, i, p.Is, mask, 0, true);
+    gateup_task<ACT, SFMT, RMAX>(p, sm, p.shared, 0, i, p.Is, mask, 0, true, 0u, false);
 }
 
 /* Shared-expert gate/up in the fused launch: workgroup g owns rows g, g + grid, ...; its waves
  * claim them one at a time from an LDS counter (sm.shared_next, zeroed beforehand), so a wave
  * that also selects joins when it is done. */
 template <int ACT, int SFMT, int RMAX>
-__device__ __forceinline__ void ph_gateup_shared_claim(const Params& p, Smem& sm) {
+__device__ __forceinline__ void ph_gateup_shared_claim(const Params& p, Smem& sm, uint32_t htag,
+                                                       bool hskip) {
   if (p.Is <= 0) return;
   const uint32_t mask = (1u << p.R) - 1u;
   for (;;) {
@@ -1353,19 +1363,21 @@ __device__ __forceinline__ void ph_gateup_shared_claim(const Params& p, Smem& sm
     const int n = __builtin_amdgcn_readfirstlane(atomicAdd(&sm.shared_next, 1)) / 64;
     const int i = (int)blockIdx.x + n * (int)gridDim.x;
     if (i >= p.Is) break;
-    gateup_task<ACT, SFMT, RMAX>(p, sm, p.shared, 0, i, p.Is, mask, 0, true);
+    gateup_task<ACT, SFMT, RMAX>(p, sm, p.shared, 0, i, p.Is, mask, 0, true, htag, hskip);
   }
 }
 
 /* Routed gate/up: task t of the nU * I tasks goes to wave t % waves of the grid, spread over
  * compute units first, so that at any moment the grid streams one contiguous stretch of rows. */
 template <int ACT, int RFMT, int RMAX>
-__device__ __forceinline__ void ph_gateup_routed(const Params& p, const Smem& sm) {
+__device__ __forceinline__ void ph_gateup_routed(const Params& p, const Smem& sm, uint32_t htag,
+                                                 bool hskip) {
   const long T = (long)sm.nU * p.I;
   const long nwt = (long)gridDim.x * kWaves;
   for (long t = wave_major_id(); t < T; t += nwt) {
     const int u = (int)(t / p.I), i = (int)(t % p.I);
-    gateup_task<ACT, RFMT, RMAX>(p, sm, p.routed, sm.U[u], i, p.I, sm.umask[u], u, false);
+    gateup_task<ACT, RFMT, RMAX>(p, sm, p.routed, sm.U[u], i, p.I, sm.umask[u], u, false, htag,
+                                 hskip);
   }
 }
 
@@ -1449,21 +1461,29 @@ __device__ __forceinline__ void down_task(const Params& p, const Smem& sm, const
 }
 
 /* Items [first, last) whose hidden rows fit in the staging area (bytes and list entries). */
-__device__ __forceinline__ int down_group_end(const Params& p, const Smem& sm, int first,
-                                              size_t ab) {
-  const int nU = sm.nU;
-  int item = first, count = 0;
+/* Order of the down phase's items: the shared expert first (its hidden rows are complete
+ * earliest), then the distinct routed experts in ascending order. */
+__device__ __forceinline__ int down_item(const Params& p, const Smem& sm, int k) {
+  return p.Is > 0 ? (k == 0 ? sm.nU : k - 1) : k;
+}
+
+/* End of the group of items [k0, end): as many as fit the staging area, at most max_items. */
+__device__ __forceinline__ int down_group_end(const Params& p, const Smem& sm, int k0, size_t ab,
+                                              int max_items) {
+  const int nU = sm.nU, n_items = nU + (p.Is > 0 ? 1 : 0);
+  int k = k0, count = 0;
   size_t used = 0;
-  while (item <= nU) {
+  while (k < n_items && k - k0 < max_items) {
+    const int item = down_item(p, sm, k);
     const int inter = item == nU ? p.Is : p.I;
     const int rows = __popc(sm.umask[item]);
     const size_t need = (size_t)rows * inter * ab;
-    if (item > first && (used + need > (size_t)kLdsHidBytes || count + rows > kMaxStaged)) break;
+    if (k > k0 && (used + need > (size_t)kLdsHidBytes || count + rows > kMaxStaged)) break;
     used += need;
     count += rows;
-    ++item;
+    ++k;
   }
-  return item;
+  return k;
 }
 
 /* Hidden-position slice of the workgroup for the down projections and the expand. */
@@ -1524,7 +1544,8 @@ __device__ __forceinline__ void slice_store(const Params& p, const Slice& c, Sme
   }
 }
 
-/* Staging list of the items [first, last): for every (item, row that uses it), in item-major
+/* Staging list of the items of positions [first, last) in down_item order: for every (item, row
+ * that uses it), in item-major
  * order, the source of the hidden row (routed [R][K][I] or shared [R][Is]), its LDS offset and
  * length in 16-byte units, and sm.voff. One wave scans the items 64 at a time. */
 __device__ __forceinline__ void stage_list(const Params& p, Smem& sm, int first, int last,
@@ -1533,9 +1554,9 @@ __device__ __forceinline__ void stage_list(const Params& p, Smem& sm, int first,
     const int lane = threadIdx.x, nU = sm.nU;
     int nv = 0;
     uint32_t off = 0;
-    for (int it0 = first; it0 < last; it0 += 64) {
-      const int it = it0 + lane;
-      const bool live = it < last;
+    for (int k0 = first; k0 < last; k0 += 64) {
+      const bool live = k0 + lane < last;
+      const int it = live ? down_item(p, sm, k0 + lane) : 0;
       const uint32_t m = live ? sm.umask[it] : 0u;
       const bool sh = it == nU;
       const uint32_t vl = (uint32_t)((size_t)(sh ? p.Is : p.I) * ab / 16);
@@ -1557,8 +1578,9 @@ __device__ __forceinline__ void stage_list(const Params& p, Smem& sm, int first,
         for (int r = 0; r < p.R; ++r)
           if (m & (1u << r)) {
             sm.voff[it][r] = (uint16_t)o;
-            sm.vsrc[v] = sh ? (uint32_t)(kHidShared | ((size_t)r * vl * 16))
-                            : (uint32_t)(((size_t)r * p.K + sm.uslot[it][r]) * vl * 16);
+            /* source: first element of the hidden row (tagged buffers) */
+            sm.vsrc[v] = sh ? (uint32_t)(kHidShared | ((size_t)r * p.Is))
+                            : (uint32_t)(((size_t)r * p.K + sm.uslot[it][r]) * p.I);
             sm.vdst[v] = (uint16_t)o;
             sm.vlen[v] = (uint16_t)vl;
             ++v;
@@ -1573,29 +1595,40 @@ __device__ __forceinline__ void stage_list(const Params& p, Smem& sm, int first,
   __syncthreads();
 }
 
-/* Copies the listed hidden rows into LDS with coherent 16-byte loads: wave w takes rows
- * w, w + 8, ...; each lane keeps up to 8 loads in flight before storing them. */
-__device__ __forceinline__ void stage_copy(const Params& p, Smem& sm, size_t ab) {
+/* Copies the listed hidden rows into LDS, dropping their tags: wave w takes rows w, w + 8, ...;
+ * a 16-byte LDS chunk (8 bf16 or 4 f32 values) comes from 32 bytes of tagged values (two
+ * coherent 16-byte loads); each lane keeps up to 4 chunks in flight before storing them. With
+ * check, a chunk whose tags are not yet `tag` is loaded again (bounded wait); on expiry the
+ * function reports once and returns false for the whole workgroup. */
+template <int ACT>
+__device__ __forceinline__ bool stage_copy(const Params& p, Smem& sm, bool check, uint32_t tag) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const __amdgpu_buffer_rsrc_t hr = coh_region(p.h_routed, (size_t)p.R * p.K * p.I * ab);
-  const __amdgpu_buffer_rsrc_t hsr = coh_region(p.h_shared, (size_t)p.R * (p.Is > 0 ? p.Is : 1) * ab);
+  constexpr int TB = ACT == F32 ? 8 : 4; /* tagged bytes per value */
+  constexpr int EPC = ACT == F32 ? 4 : 8; /* values per 16-byte LDS chunk */
+  const __amdgpu_buffer_rsrc_t hr = coh_region(p.h_routed, (size_t)p.R * p.K * p.I * TB);
+  const __amdgpu_buffer_rsrc_t hsr = coh_region(p.h_shared, (size_t)p.R * (p.Is > 0 ? p.Is : 1) * TB);
+  if (threadIdx.x == 0) sm.sel_ok = 1;
+  __syncthreads();
   const int nv = sm.nv;
   int v = wave, ch = lane;
   while (v < nv && ch >= (int)sm.vlen[v]) {
     v += kWaves;
     ch = lane;
   }
-  constexpr int B = 8;
+  bool ok = true;
+  constexpr int B = 4;
   while (__ballot(v < nv) != 0ull) {
-    uint4 buf[B];
-    uint32_t dst[B];
+    uint4 lo[B], hi[B];
+    uint32_t dst[B], src[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       dst[b] = 0xFFFFFFFFu;
       if (v < nv) {
-        const uint32_t src = sm.vsrc[v];
-        buf[b] = (src & kHidShared) ? coh_b128(hsr, (src & ~kHidShared) + ch * 16)
-                                    : coh_b128(hr, src + ch * 16);
+        const uint32_t s0 = sm.vsrc[v];
+        src[b] = ((s0 & ~kHidShared) + (uint32_t)ch * EPC) * TB | (s0 & kHidShared);
+        const __amdgpu_buffer_rsrc_t rs = (s0 & kHidShared) ? hsr : hr;
+        lo[b] = coh_b128(rs, src[b] & ~kHidShared);
+        hi[b] = coh_b128(rs, (src[b] & ~kHidShared) + 16);
         dst[b] = (uint32_t)sm.vdst[v] + ch;
         ch += 64;
         while (v < nv && ch >= (int)sm.vlen[v]) {
@@ -1605,68 +1638,106 @@ __device__ __forceinline__ void stage_copy(const Params& p, Smem& sm, size_t ab)
       }
     }
 #pragma unroll
-    for (int b = 0; b < B; ++b)
-      if (dst[b] != 0xFFFFFFFFu) reinterpret_cast<uint4*>(sm.big)[dst[b]] = buf[b];
+    for (int b = 0; b < B; ++b) {
+      if (dst[b] == 0xFFFFFFFFu) continue;
+      if (check) {
+        auto stale = [&]() {
+          if (ACT == F32)
+            return lo[b].y != tag || lo[b].w != tag || hi[b].y != tag || hi[b].w != tag;
+          const uint32_t w0 = lo[b].x & lo[b].y & lo[b].z & lo[b].w & hi[b].x & hi[b].y & hi[b].z & hi[b].w;
+          const uint32_t w1 = lo[b].x | lo[b].y | lo[b].z | lo[b].w | hi[b].x | hi[b].y | hi[b].z | hi[b].w;
+          return (w0 >> 16) != tag || (w1 >> 16) != tag;
+        };
+        if (stale()) {
+          const __amdgpu_buffer_rsrc_t rs = (src[b] & kHidShared) ? hsr : hr;
+          const uint32_t off = src[b] & ~kHidShared;
+          const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+          while (stale()) {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_sleep(1);
+            lo[b] = coh_b128(rs, off);
+            hi[b] = coh_b128(rs, off + 16);
+            if (__builtin_amdgcn_s_memrealtime() - t0 > sm.spin) {
+              ok = false;
+              break;
+            }
+          }
+        }
+      }
+      uint4 o;
+      if (ACT == F32) {
+        o = make_uint4(lo[b].x, lo[b].z, hi[b].x, hi[b].z);
+      } else {
+        o = make_uint4((lo[b].x & 0xFFFFu) | (lo[b].y << 16), (lo[b].z & 0xFFFFu) | (lo[b].w << 16),
+                       (hi[b].x & 0xFFFFu) | (hi[b].y << 16), (hi[b].z & 0xFFFFu) | (hi[b].w << 16));
+      }
+      reinterpret_cast<uint4*>(sm.big)[dst[b]] = o;
+    }
   }
+  if (!ok) sm.sel_ok = 0;
   __syncthreads();
+  if (sm.sel_ok == 0) {
+    if (threadIdx.x == 0) report_timeout(p, PH_GATEUP);
+    return false;
+  }
+  return true;
 }
 
-/* In the fused launch (FUSED), the wait for the gate/up barrier runs after this wave has issued
- * the loads of its first routed task (so they overlap the wait) and before any hidden row is
- * read. */
+/* Items are processed in groups (down_item order); each group's hidden rows are staged in LDS,
+ * then its tasks (item, kRG output rows of the slice) run one per wave. In the fused launch the
+ * first group holds at most kFusedGroupItems items and every staging waits (bounded) for the
+ * tags of this launch: no grid barrier separates gate/up from down, so a workgroup starts on the
+ * first items while others still finish their gate/up rows. Before a group is staged, each wave
+ * issues the weight loads of its first routed task (one row). */
+constexpr int kFusedGroupItems = 3;
+
 template <int ACT, int RFMT, int SFMT, int RMAX, bool FUSED>
-__device__ __forceinline__ bool ph_down(const Params& p, Smem& sm) {
+__device__ __forceinline__ bool ph_down(const Params& p, Smem& sm, uint32_t htag) {
   const int tid = threadIdx.x, wave = tid >> 6;
   const DownGeo g = down_geo(p, sm);
   const int nU = sm.nU, R = p.R;
   const size_t ab = ACT == F32 ? 4 : 2;
   const int nq = (g.nh + kRG - 1) / kRG;
   constexpr int CHR = Fmt<RFMT>::CH_DN;
-  /* prefetch: first task of this wave in the first group, if routed */
-  int last = down_group_end(p, sm, 0, ab);
-  WRegs<RFMT, kRG, CHR> pre;
+  const int n_items = nU + (p.Is > 0 ? 1 : 0);
   WRegs<SFMT, kRG, Fmt<SFMT>::CH_DN> none;
-  bool have_pre = false;
-  /* wave 0 polls the gate/up barrier: it issues no early loads that its polls would wait on */
-  if (RMAX == 1 && wave > 0 && wave < last * nq && wave / nq < nU) {
-    const uint8_t* vr[kRG];
-    const uint8_t* sr[kRG];
-    down_rows<ACT, RFMT>(p, g, p.routed, sm.U[wave / nq], p.I, wave % nq, vr, sr);
-    wregs_load(pre, vr, sr, p.I, 0);
-    have_pre = true;
-  }
-  if (FUSED) {
-    /* the expand's slice inputs and the staging list need nothing from the other workgroups:
-     * both are prepared while the last ones finish their gate/up rows */
-    const Slice c = slice_of(p);
-    SliceRegs sreg;
-    slice_prefetch<ACT>(p, c, sreg);
-    stage_list(p, sm, 0, last, ab);
-    if (!bar_wait(p, sm, PH_GATEUP)) return false;
-    slice_store(p, c, sm, sreg);
-    stamp(p, sm.trace_on != 0, 10);
-  }
-  int first = 0;
-  while (first <= nU) {
-    if (first > 0) last = down_group_end(p, sm, first, ab);
-    if (first > 0 || !FUSED) {
-      __syncthreads(); /* the previous group's tasks are done with the staging area */
-      stage_list(p, sm, first, last, ab);
-    }
-    stage_copy(p, sm, ab);
-    if (FUSED && first == 0) stamp(p, sm.trace_on != 0, 21);
-    const int ntask = (last - first) * nq;
-    for (int t = wave; t < ntask; t += kWaves) {
-      const int it = first + t / nq, q = t % nq;
-      if (it == nU) {
-        if (p.Is > 0 && sm.umask[it])
-          down_task<ACT, SFMT, RMAX>(p, sm, g, p.shared, 0, p.Is, it, q, true, none, false);
-      } else {
-        const bool use_pre = have_pre && first == 0 && t == wave;
-        down_task<ACT, RFMT, RMAX>(p, sm, g, p.routed, sm.U[it], p.I, it, q, false, pre, use_pre);
+  const Slice c = slice_of(p);
+  SliceRegs sreg;
+  if (FUSED) slice_prefetch<ACT>(p, c, sreg);
+  int k0 = 0;
+  while (k0 < n_items) {
+    /* fused: a small first group (ready earliest), then groups as large as the staging area */
+    const int k1 = down_group_end(p, sm, k0, ab, FUSED && k0 == 0 ? kFusedGroupItems : n_items);
+    if (k0 > 0) __syncthreads(); /* the previous group's tasks are done with the staging area */
+    stage_list(p, sm, k0, k1, ab);
+    const int ntask = (k1 - k0) * nq;
+    WRegs<RFMT, kRG, CHR> pre;
+    bool have_pre = false;
+    /* (one row, bf16 weights: the other formats' decode needs the registers) */
+    if (RMAX == 1 && RFMT == BF16 && wave < ntask) {
+      const int it = down_item(p, sm, k0 + wave / nq);
+      if (it != nU) {
+        const uint8_t* vr[kRG];
+        const uint8_t* sr[kRG];
+        down_rows<ACT, RFMT>(p, g, p.routed, sm.U[it], p.I, wave % nq, vr, sr);
+        wregs_load(pre, vr, sr, p.I, 0);
+        have_pre = true;
       }
     }
-    first = last;
+    if (!stage_copy<ACT>(p, sm, FUSED, htag)) return false;
+    if (FUSED && k0 == 0) {
+      slice_store(p, c, sm, sreg);
+      stamp(p, sm.trace_on != 0, 21);
+    }
+    for (int t = wave; t < ntask; t += kWaves) {
+      const int it = down_item(p, sm, k0 + t / nq), q = t % nq;
+      if (it == nU)
+        down_task<ACT, SFMT, RMAX>(p, sm, g, p.shared, 0, p.Is, it, q, true, none, false);
+      else
+        down_task<ACT, RFMT, RMAX>(p, sm, g, p.routed, sm.U[it], p.I, it, q, false, pre,
+                                   have_pre && t == wave);
+    }
+    k0 = k1;
   }
   __syncthreads();
   /* combine */
@@ -1735,8 +1806,11 @@ __device__ __forceinline__ bool reduce_carry(const Params& p, Smem& sm, int q, b
 }
 
 /* End-of-launch arrival (no data is published by it): advances this workgroup's end counter
- * once per fused launch, which the next launch reads as its epoch. */
-__device__ __forceinline__ void end_arrive(const Params& p) {
+ * once per fused launch, which the next launch reads as its epoch. Every workgroup must have read
+ * the end counters before any advances them: without a carry the mix barrier (passed by then)
+ * guarantees it; with a carry the mix arrivals are waited for here (long complete). */
+__device__ __forceinline__ void end_arrive(const Params& p, Smem& sm) {
+  if (p.carry_in && !bar_wait(p, sm, PH_MIX)) return;
   __syncthreads();
   if (threadIdx.x == 0)
     __hip_atomic_fetch_add(bar_counter(p, PH_END, blockIdx.x % kBarGroups), (uint64_t)1,
@@ -1780,7 +1854,7 @@ __device__ __forceinline__ void ph_expand(const Params& p, Smem& sm, const float
     }
   }
   if (p.w_mix_next == nullptr) {
-    if (FUSED) end_arrive(p);
+    if (FUSED) end_arrive(p, sm);
     return;
   }
   stamp(p, sm.trace_on != 0, 12);
@@ -1826,7 +1900,7 @@ __device__ __forceinline__ void ph_expand(const Params& p, Smem& sm, const float
            ((uint64_t)tag << 32) | __float_as_uint(t));
   }
   if (FUSED) {
-    end_arrive(p);
+    end_arrive(p, sm);
     for (int q = blockIdx.x; q < R * kNCarry; q += gridDim.x)
       if (!reduce_carry(p, sm, q, true, tag)) return;
   } else if (arrive_last_single(p, sm)) {
@@ -1878,7 +1952,7 @@ __global__ void __launch_bounds__(kBlock) k_gateup(Params p) {
   load_selection(p, sm);
   ph_plan(p, sm);
   ph_gateup_shared<ACT, SFMT, RMAX>(p, sm);
-  ph_gateup_routed<ACT, RFMT, RMAX>(p, sm);
+  ph_gateup_routed<ACT, RFMT, RMAX>(p, sm, 0u, false);
 }
 
 template <int ACT, int RFMT, int SFMT, int RMAX>
@@ -1887,7 +1961,7 @@ __global__ void __launch_bounds__(kBlock) k_down(Params p) {
   if (threadIdx.x == 0) sm.trace_on = 0;
   load_selection(p, sm);
   ph_plan(p, sm);
-  ph_down<ACT, RFMT, SFMT, RMAX, false>(p, sm);
+  ph_down<ACT, RFMT, SFMT, RMAX, false>(p, sm, 0u);
 }
 
 template <int ACT, int RMAX>
@@ -1963,17 +2037,19 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   ph_sinkhorn(p, sm, blockIdx.x == 0); /* comb is needed only by the expand */
   select_rows(p, sm, blockIdx.x == 0, true, tag);
   stamp(p, tr, 6);
-  ph_gateup_shared_claim<ACT, SFMT, RMAX>(p, sm);
+  /* hidden rows carry a 16-bit tag of this launch (never 0, the value the init leaves) */
+  const uint32_t htag = (uint32_t)(sm.epoch % 65535u) + 1u;
+  const bool hskip = sm.skip_phase == PH_GATEUP; /* fault injection: store no hidden rows */
+  ph_gateup_shared_claim<ACT, SFMT, RMAX>(p, sm, htag, hskip);
   stamp(p, tr, 5);
   __syncthreads();
   if (!select_finish(p, sm, blockIdx.x == 0)) return;
   stamp(p, tr, 7);
   ph_plan(p, sm);
   stamp(p, tr, 8);
-  ph_gateup_routed<ACT, RFMT, RMAX>(p, sm);
+  ph_gateup_routed<ACT, RFMT, RMAX>(p, sm, htag, hskip);
   stamp(p, tr, 9);
-  bar_arrive(p, sm, PH_GATEUP);
-  if (!ph_down<ACT, RFMT, SFMT, RMAX, true>(p, sm)) return;
+  if (!ph_down<ACT, RFMT, SFMT, RMAX, true>(p, sm, htag)) return;
   stamp(p, tr, 11);
   const DownGeo g = down_geo(p, sm);
   ph_expand<ACT, RMAX, true>(p, sm, g.blk);

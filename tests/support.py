@@ -73,6 +73,16 @@ def d2h(t, dtype, shape) -> np.ndarray:
     return a[:n].view(dtype).reshape(shape).copy()
 
 
+def hidden_rows(shape: mono.Shape, ws, which: int, adt, dims) -> np.ndarray:
+    """Hidden rows (MONO_T_H_ROUTED / MONO_T_H_SHARED) without their tags: each value is stored
+    beside the launch tag (bf16 in the low half of a uint32, f32 in the low half of a uint64)."""
+    if adt == np.uint16:
+        raw = ws_tensor(shape, ws, which, np.uint32, dims)
+        return (raw & 0xFFFF).astype(np.uint16)
+    raw = ws_tensor(shape, ws, which, np.uint64, dims)
+    return (raw & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+
+
 def ws_tensor(shape: mono.Shape, ws, which: int, dtype, dims) -> np.ndarray:
     p, n = mono.mono_workspace_tensor(shape, ws, which)
     buf = np.empty(int(np.prod(dims)), dtype)
@@ -134,8 +144,8 @@ class Gpu:
             weights=d2h(b["weights"], np.float32, (R, K)), shared=d2h(b["shared"], adt, (R, H)),
             routed=d2h(b["routed"], np.float32, (R, H)), block=d2h(b["block"], adt, (R, H)),
             new_state=d2h(b["new"], adt, (R, 4, H)))
-        out["h_routed"] = ws_tensor(s, self.ws, mono.MONO_T_H_ROUTED, adt, (R, K, I))
-        out["h_shared"] = (ws_tensor(s, self.ws, mono.MONO_T_H_SHARED, adt, (R, Is)) if Is > 0
+        out["h_routed"] = hidden_rows(s, self.ws, mono.MONO_T_H_ROUTED, adt, (R, K, I))
+        out["h_shared"] = (hidden_rows(s, self.ws, mono.MONO_T_H_SHARED, adt, (R, Is)) if Is > 0
                            else np.zeros((R, 0), adt))
         if w_next is not None:
             out["carry"] = d2h(b["carry"], np.float32, (R, 25))
@@ -164,8 +174,9 @@ class Gpu:
             logits=T(mono.MONO_T_LOGITS, np.float32, (R, E)),
             idx=T(mono.MONO_T_IDX, np.int32, (R, K)),
             weights=T(mono.MONO_T_WEIGHTS, np.float32, (R, K)),
-            h_routed=T(mono.MONO_T_H_ROUTED, adt, (R, K, I)),
-            h_shared=(T(mono.MONO_T_H_SHARED, adt, (R, Is)) if Is > 0 else np.zeros((R, 0), adt)),
+            h_routed=hidden_rows(s, ws, mono.MONO_T_H_ROUTED, adt, (R, K, I)),
+            h_shared=(hidden_rows(s, ws, mono.MONO_T_H_SHARED, adt, (R, Is)) if Is > 0
+                      else np.zeros((R, 0), adt)),
             shared=T(mono.MONO_T_SHARED, adt, (R, H)),
             routed=T(mono.MONO_T_ROUTED, np.float32, (R, H)),
             block=T(mono.MONO_T_BLOCK, adt, (R, H)),
