@@ -180,7 +180,7 @@ Params base_params(const mono_shape* s, const mono_layer* L, void* ws, int grid)
   const WsLayout W = ws_layout(*s);
   uint8_t* b = static_cast<uint8_t*>(ws);
   p.ctl = reinterpret_cast<uint32_t*>(b + W.ctl);
-  p.mix_part = reinterpret_cast<float*>(b + W.mix_part);
+  p.mix_part = reinterpret_cast<uint64_t*>(b + W.mix_part);
   p.carry_part = reinterpret_cast<float*>(b + W.carry_part);
   p.lgp = reinterpret_cast<uint64_t*>(b + W.lgp);
   p.trace = reinterpret_cast<uint64_t*>(b + W.trace);

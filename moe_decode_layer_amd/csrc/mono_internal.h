@@ -27,22 +27,20 @@ constexpr uint32_t kDefaultSpin = 200000000u; /* 2 s of the 100 MHz real-time co
 
 /* Control words at the head of the workspace (u32 indices). */
 enum {
-  CTL_BAR_COUNT = 0,
-  CTL_BAR_GEN = 1,
-  CTL_CARRY_COUNT = 2,
   CTL_ERR = 8,       /* 4 words: flag, phase, workgroup, count */
   CTL_SPIN = 16,     /* bounded-wait limit in real-time ticks (0 = default) */
-  CTL_FAULT_WG = 17, /* workgroup that skips a barrier arrival (-1 = none) */
+  CTL_FAULT_WG = 17, /* workgroup that withholds its published values (-1 = none) */
   CTL_FAULT_PHASE = 18,
   CTL_TRACE = 19,    /* nonzero: the fused launch records per-phase timestamps */
   CTL_XEND64 = 60,   /* uint64 arrival counter of the unfused expand (last-arriver election) */
-  CTL_BAR64 = 64,    /* 4 barriers x 8 groups of uint64 arrival counters, never reset */
+  CTL_BAR64 = 64,    /* uint64 counters [phase - 1][8 groups], never reset (only PH_END used) */
   CTL_WORDS = 128
 };
 
-/* Barrier phases (also reported in the error word). */
+/* Points where the fused launch's workgroups exchange values (reported in the error word and
+ * named by fault injection); PH_END also indexes the end counters that give the launch epoch. */
 enum { PH_MIX = 1, PH_ROUTER = 2, PH_GATEUP = 3, PH_END = 4 };
-constexpr int kBarGroups = 8; /* one arrival counter per group of workgroups (blockIdx % 8) */
+constexpr int kBarGroups = 8; /* one end counter per group of workgroups (blockIdx % 8) */
 
 struct Mat {
   int fmt;
@@ -96,7 +94,7 @@ struct Params {
   float* carry_out;
   float* carry_ws;   /* workspace copy of the carry */
   /* workspace scratch */
-  float* mix_part;   /* [nchunk][R][25] */
+  uint64_t* mix_part; /* [nchunk][R][25] tagged mix partial sums: value bits | tag << 32 */
   float* carry_part; /* [R * 25][grid] tagged partials: value bits | epoch tag << 32 */
   uint64_t* lgp;     /* [parts][R][E] tagged router logit parts (same format) */
   uint64_t* trace;   /* [grid][32] real-time stamps */
@@ -139,8 +137,8 @@ inline WsLayout ws_layout(const mono_shape& s) {
     return at;
   };
   L.ctl = take(CTL_WORDS * 4);
-  L.mix_part = take(nchunk * R * kNCarry * 4);
   L.carry_part = take((size_t)kMaxGrid * R * kNCarry * 8);
+  L.mix_part = take(nchunk * R * kNCarry * 8);
   L.lgp = take(router_parts(s.hidden) * R * E * 8);
   /* hidden rows, tagged: each value with the launch tag beside it (bf16 | tag16 << 16 in a
    * uint32, or f32 | tag32 << 32 in a uint64) */

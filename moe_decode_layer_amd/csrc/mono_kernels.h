@@ -160,6 +160,52 @@ __device__ __forceinline__ uint2 coh_b64(__amdgpu_buffer_rsrc_t r, uint32_t off)
   return make_uint2(v[0], v[1]);
 }
 
+/* Copies n tagged values (value bits | tag << 32, uint64) at src into LDS as floats at dst with
+ * the whole workgroup, two values per 16-byte coherent load. With check, a pair whose tags are
+ * not yet `tag` is loaded again (bounded by spin ticks); returns false (uniform) on expiry. */
+__device__ __forceinline__ bool coh_copy_tagged_to_lds(const uint64_t* src, int n, float* dst,
+                                                       bool check, uint32_t tag, uint32_t spin,
+                                                       int* flag) {
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t r = coh_region(src, (size_t)n * 8);
+  const int npair = (n + 1) / 2;
+  if (tid == 0) *flag = 1;
+  __syncthreads();
+  bool ok = true;
+  constexpr int B = 4;
+  for (int v0 = 0; v0 < npair; v0 += B * kBlock) {
+    uint4 buf[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int v = v0 + b * kBlock + tid;
+      if (v < npair) buf[b] = coh_b128(r, (uint32_t)v * 16u);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int v = v0 + b * kBlock + tid;
+      if (v >= npair) continue;
+      const bool two = 2 * v + 1 < n;
+      if (check && (buf[b].y != tag || (two && buf[b].w != tag))) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (buf[b].y != tag || (two && buf[b].w != tag)) {
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_sleep(1);
+          buf[b] = coh_b128(r, (uint32_t)v * 16u);
+          if (__builtin_amdgcn_s_memrealtime() - t0 > spin) {
+            ok = false;
+            break;
+          }
+        }
+      }
+      dst[2 * v] = __uint_as_float(buf[b].x);
+      if (two) dst[2 * v + 1] = __uint_as_float(buf[b].z);
+    }
+  }
+  if (!ok) *flag = 0;
+  __syncthreads();
+  return *flag != 0;
+}
+
 /* Waits until this wave's memory operations have completed (and orders the compiler). */
 __device__ __forceinline__ void drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -440,18 +486,17 @@ struct Smem {
 };
 
 /* ------------------------------------------------------------------------------------------
- * Device-wide barriers, split into arrive and wait so that independent work can run between
- * them. Each barrier has a 64-bit arrival counter that is never reset: a workgroup completes
- * its stores, then adds 1 (no return value needed). At launch start every workgroup reads the
- * counters; since a barrier cannot complete before every workgroup has arrived, the count it
- * reads is below (epoch + 1) * grid for the epoch of this launch, so epoch = count / grid and
- * the barrier completes when the count reaches (epoch + 1) * grid. Waits are bounded: on
- * expiry the error word is set and every thread of the workgroup gets false (the workspace then
- * needs mono_workspace_init). Fault injection: workgroup fault_wg skips its arrival at
- * fault_phase. */
+ * Ordering between the workgroups of the fused launch. There is no grid barrier: every value a
+ * workgroup publishes for others (mix partials, router logit parts, hidden rows, carry partials)
+ * is stored with a tag of the launch beside it, and the reader waits until the tags are
+ * current. The tag comes from the launch epoch: each workgroup adds 1 to an end counter (one
+ * of 8 groups, by blockIdx % 8) when it finishes, so at the start of a launch the counters hold
+ * epoch * (workgroups of the group) and epoch = count / ceil(grid / 8). Waits are bounded: on
+ * expiry the error word is set and the workgroup returns (the workspace then needs
+ * mono_workspace_init). Fault injection: workgroup fault_wg withholds its values at fault_phase. */
 
-/* Counter of `group` for barrier `phase`. Workgroup w arrives on group w % 8, so 32 (not 256)
- * arrivals contend for one address; a waiter reads the 8 counters in parallel. */
+/* Counter of `group` for `phase` (only PH_END has one). Workgroup w uses group w % 8, so 32
+ * (not 256) arrivals contend for one address. */
 __device__ __forceinline__ uint64_t* bar_counter(const Params& p, int phase, int group) {
   return reinterpret_cast<uint64_t*>(p.ctl + CTL_BAR64) + (phase - 1) * kBarGroups + group;
 }
@@ -466,12 +511,9 @@ __device__ __forceinline__ void report_timeout(const Params& p, int phase) {
 }
 
 /* Reads the launch epoch and debug words once per launch (made visible to the workgroup by the
- * next __syncthreads). Every fused launch advances every barrier counter of group g by exactly
- * n_g = ceil((grid - g) / 8) (a launch given a carry still arrives at the mix barrier), and the
- * end counters advance only after every workgroup has passed the gate/up barrier, hence after
- * every workgroup has started and read them here. So at launch start each end counter holds
- * epoch * n_g exactly, and every barrier of this launch completes when each group counter
- * reaches (epoch + 1) * n_g. */
+ * next __syncthreads). Every fused launch advances end counter g by exactly
+ * n_g = ceil((grid - g) / 8), and no workgroup finishes before every workgroup has started and
+ * read the counters (see end_arrive), so at launch start end counter 0 holds epoch * n_0. */
 __device__ __forceinline__ void bar_setup(const Params& p, Smem& sm) {
   if (threadIdx.x == 0) {
     sm.trace_on = ld_coh(p.ctl + CTL_TRACE) != 0u;
@@ -483,43 +525,6 @@ __device__ __forceinline__ void bar_setup(const Params& p, Smem& sm) {
     sm.spin = spin ? spin : kDefaultSpin;
     sm.skip_phase = (int32_t)fwg == (int32_t)blockIdx.x ? (int)fph : -1;
   }
-}
-
-__device__ __forceinline__ uint64_t bar_target(const Smem& sm, int g) {
-  const uint64_t n = ((uint64_t)gridDim.x - g + kBarGroups - 1) / kBarGroups;
-  return (sm.epoch + 1) * n;
-}
-
-__device__ __forceinline__ void bar_arrive(const Params& p, Smem& sm, int phase) {
-  drain();
-  __syncthreads();
-  if (threadIdx.x == 0 && sm.skip_phase != phase)
-    __hip_atomic_fetch_add(bar_counter(p, phase, blockIdx.x % kBarGroups), (uint64_t)1,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ bool bar_wait(const Params& p, Smem& sm, int phase) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int g = lane < kBarGroups ? lane : 0;
-    const uint64_t* cnt = bar_counter(p, phase, g);
-    const uint64_t target = bar_target(sm, g);
-    int ok = 1;
-    if (__ballot(lane < kBarGroups && ld_coh(cnt) < target) != 0ull) {
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (__ballot(lane < kBarGroups && ld_coh(cnt) < target) != 0ull) {
-        __builtin_amdgcn_s_sleep(1);
-        if (__builtin_amdgcn_s_memrealtime() - t0 > sm.spin) {
-          if (lane == 0) report_timeout(p, phase);
-          ok = 0;
-          break;
-        }
-      }
-    }
-    if (lane == 0) sm.flag = ok;
-  }
-  __syncthreads();
-  return sm.flag != 0;
 }
 
 /* Last-arriver election of a plain (non-persistent) launch: one counter that every launch
@@ -555,7 +560,7 @@ __device__ __forceinline__ int wave_major_id() {
  * elements of the flattened row) is one wave task: part[t][r][j] = W_mix[j] . s over the chunk,
  * part[t][r][24] = sum s^2 over the chunk. */
 template <int ACT, int RMAX>
-__device__ __forceinline__ void ph_mix_partials(const Params& p) {
+__device__ __forceinline__ void ph_mix_partials(const Params& p, uint32_t tag, bool skip) {
   const int n = 4 * p.H, nch = n / kMixChunk;
   const int lane = threadIdx.x & 63;
   const int nwt = gridDim.x * kWaves;
@@ -578,7 +583,7 @@ __device__ __forceinline__ void ph_mix_partials(const Params& p) {
       s[0] = bf2f(v.x & 0xFFFFu); s[1] = bf2f(v.x >> 16);
       s[2] = bf2f(v.y & 0xFFFFu); s[3] = bf2f(v.y >> 16);
     }
-    float* out = p.mix_part + ((size_t)ch * p.R + r) * kNCarry;
+    uint64_t* out = p.mix_part + ((size_t)ch * p.R + r) * kNCarry;
 #pragma unroll
     for (int j = 0; j < kNMix; ++j) {
       float a = w[j].x * s[0];
@@ -586,14 +591,14 @@ __device__ __forceinline__ void ph_mix_partials(const Params& p) {
       a = fmaf(w[j].z, s[2], a);
       a = fmaf(w[j].w, s[3], a);
       const float tot = wave_sum(a);
-      if (lane == 0) stf_coh(out + j, tot);
+      if (lane == 0 && !skip) st_coh(out + j, ((uint64_t)tag << 32) | __float_as_uint(tot));
     }
     float ss = s[0] * s[0];
     ss = fmaf(s[1], s[1], ss);
     ss = fmaf(s[2], s[2], ss);
     ss = fmaf(s[3], s[3], ss);
     const float tot = wave_sum(ss);
-    if (lane == 0) stf_coh(out + kNMix, tot);
+    if (lane == 0 && !skip) st_coh(out + kNMix, ((uint64_t)tag << 32) | __float_as_uint(tot));
   }
 }
 
@@ -634,16 +639,23 @@ __device__ __forceinline__ void load_bias(const Params& p, Smem& sm) {
  * + b[4+i]); comb = Sinkhorn on exp(a2 m[8+4i+j] + b[8+4i+j] - max), rows then columns.
  * Needs load_pre_params first (and a __syncthreads between). */
 template <int ACT, int RMAX>
-__device__ __forceinline__ void ph_hc_pre(const Params& p, Smem& sm, bool write_out) {
+__device__ __forceinline__ bool ph_hc_pre(const Params& p, Smem& sm, bool write_out, bool check,
+                                          uint32_t tag) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = p.R, H = p.H, n = 4 * H, nch = n / kMixChunk;
   constexpr int VE = ACT == F32 ? 4 : 8; /* elements per 16-byte state load */
   const size_t ab = ACT == F32 ? 4 : 2;
-  /* raw mix sums: the partials [chunk][row][25] are copied into LDS with contiguous 16-byte
-   * coherent loads (one pass over 8 KB per row), then one wave per (row, output) sums them,
-   * lanes taking chunks t = lane + 64 m */
+  /* raw mix sums: the tagged partials [chunk][row][25] are copied into LDS with contiguous
+   * 16-byte coherent loads (in the fused launch once their tags are current: no grid barrier),
+   * then one wave per (row, output) sums them, lanes taking chunks t = lane + 64 m */
   float* part = reinterpret_cast<float*>(sm.big); /* free until x is written below */
-  if (!p.carry_in) coh_copy_to_lds(p.mix_part, (size_t)nch * R * kNCarry * 4, sm.big);
+  if (!p.carry_in) {
+    if (!coh_copy_tagged_to_lds(p.mix_part, nch * R * kNCarry, part, check, tag, sm.spin,
+                                &sm.flag)) {
+      if (threadIdx.x == 0) report_timeout(p, PH_MIX);
+      return false;
+    }
+  }
   __syncthreads();
   for (int q = wave; q < R * kNCarry; q += kWaves) {
     const int r = q / kNCarry, j = q % kNCarry;
@@ -805,6 +817,7 @@ __device__ __forceinline__ void ph_hc_pre(const Params& p, Smem& sm, bool write_
     }
   }
   __syncthreads();
+  return true;
 }
 
 /* comb = Sinkhorn(exp(a2 m[8 + 4 i + j] + b[8 + 4 i + j] - max)) for every row, run by waves
@@ -1806,11 +1819,11 @@ __device__ __forceinline__ bool reduce_carry(const Params& p, Smem& sm, int q, b
 }
 
 /* End-of-launch arrival (no data is published by it): advances this workgroup's end counter
- * once per fused launch, which the next launch reads as its epoch. Every workgroup must have read
- * the end counters before any advances them: without a carry the mix barrier (passed by then)
- * guarantees it; with a carry the mix arrivals are waited for here (long complete). */
+ * once per fused launch, which the next launch reads as its epoch. Every workgroup reads the end
+ * counters at its start; the persistent grid is co-resident (one workgroup per compute unit,
+ * which the tagged waits between workgroups already require), so every workgroup has started,
+ * and read them, before any workgroup can finish. */
 __device__ __forceinline__ void end_arrive(const Params& p, Smem& sm) {
-  if (p.carry_in && !bar_wait(p, sm, PH_MIX)) return;
   __syncthreads();
   if (threadIdx.x == 0)
     __hip_atomic_fetch_add(bar_counter(p, PH_END, blockIdx.x % kBarGroups), (uint64_t)1,
@@ -1913,7 +1926,7 @@ __device__ __forceinline__ void ph_expand(const Params& p, Smem& sm, const float
 
 template <int ACT, int RMAX>
 __global__ void __launch_bounds__(kBlock) k_mix_partials(Params p) {
-  ph_mix_partials<ACT, RMAX>(p);
+  ph_mix_partials<ACT, RMAX>(p, 0u, false);
 }
 
 template <int ACT, int RMAX>
@@ -1922,7 +1935,7 @@ __global__ void __launch_bounds__(kBlock) k_hc_pre(Params p) {
   if (threadIdx.x == 0) sm.trace_on = 0;
   load_pre_params<ACT>(p, sm);
   __syncthreads();
-  ph_hc_pre<ACT, RMAX>(p, sm, true);
+  ph_hc_pre<ACT, RMAX>(p, sm, true, false, 0u);
   ph_sinkhorn(p, sm, true);
 }
 
@@ -2006,30 +2019,24 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   __syncthreads();
   const bool tr = sm.trace_on != 0;
   stamp(p, tr, 0);
+  /* values exchanged between workgroups carry this launch's tag: no grid barrier */
+  const uint32_t tag = (uint32_t)(sm.epoch + 1);
   RouterRegs rpre;
   if (!p.carry_in) {
-    ph_mix_partials<ACT, RMAX>(p);
+    ph_mix_partials<ACT, RMAX>(p, tag, sm.skip_phase == PH_MIX);
     stamp(p, tr, 1);
-    bar_arrive(p, sm, PH_MIX);
-  } else {
-    bar_arrive(p, sm, PH_MIX); /* keeps every barrier counter advancing once per launch */
   }
   router_prefetch(p, rpre);
   load_pre_params<ACT>(p, sm);
   load_bias(p, sm);
-  if (!p.carry_in) {
-    if (!bar_wait(p, sm, PH_MIX)) return;
-  } else {
-    __syncthreads();
-  }
-  stamp(p, tr, 2);
   if (threadIdx.x == 0) {
     sm.sel_ok = 1;
     sm.shared_next = 0;
   }
-  ph_hc_pre<ACT, RMAX>(p, sm, blockIdx.x == 0); /* its barriers publish the two words above */
+  __syncthreads();
+  stamp(p, tr, 2);
+  if (!ph_hc_pre<ACT, RMAX>(p, sm, blockIdx.x == 0, true, tag)) return;
   stamp(p, tr, 3);
-  const uint32_t tag = (uint32_t)(sm.epoch + 1);
   /* router parts (waves 1 ..), then the select (waves 0 .. R - 1, polling the tagged logits),
    * then the shared expert's gate/up rows, claimed by whichever waves are free */
   ph_router<ACT, RMAX, true>(p, sm, rpre, tag, sm.skip_phase == PH_ROUTER);

@@ -1,8 +1,8 @@
-"""Failure handling of the persistent launch, forced from the host: workgroup 0 skips its
-arrival at a grid barrier (or, for the router, the store of its tagged logit parts) and the wait
-limit is shortened, so every waiting workgroup's bounded wait expires, the error word is set and
-the launch ends normally (no hang, no fault). After mono_workspace_init the workspace works
-again and gives the same bytes as a fresh one."""
+"""Failure handling of the persistent launch, forced from the host: workgroup 0 withholds the
+values it publishes for the other workgroups (its mix partial sums, router logit parts or hidden
+rows) and the wait limit is shortened, so every waiting workgroup's bounded wait expires, the
+error word is set and the launch ends normally (no hang, no fault). After mono_workspace_init
+the workspace works again and gives the same bytes as a fresh one."""
 
 import numpy as np
 import pytest
@@ -16,17 +16,17 @@ SMALL = synth.CONFIGS[2].with_(hidden=512, n_experts=32, top_k=4, inter=256, sha
 
 
 @pytest.mark.parametrize("phase", [PH_MIX, PH_ROUTER, PH_GATEUP])
-def test_skipped_arrival_times_out_and_recovers(phase):
+def test_withheld_values_time_out_and_recover(phase):
     import torch
     import support
     import moe_decode_layer_amd as mono
-    print("skipped arrival at barrier", phase, flush=True)
+    print("values withheld at point", phase, flush=True)
     g = support.Gpu(SMALL, layers=(0, 1))
     st = g.state(0)
     wn = g.layers[1]["w_mix"]
     ref = g.fused(st, 0, None, wn)
     grid = mono.mono_grid_size()
-    # 2 ms limit (100 MHz counter); workgroup 0 never arrives at `phase` (it has router work)
+    # 2 ms limit (100 MHz counter); workgroup 0 (it has mix, router and gate/up work) withholds
     mono.mono_workspace_set_debug(g.ws, 200000, 0, phase, support.stream())
     new = g.buf(SMALL.rows * 4 * SMALL.hidden * 2)
     carry = g.buf(SMALL.rows * 25 * 4)
