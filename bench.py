@@ -5,8 +5,9 @@ collapse + RMSNorm -> router + top-k -> shared and routed SwiGLU experts -> bloc
 carry of the next layer half's mix sums, as ONE persistent launch, with inputs resident in HBM.
 
 Headline workload: the V4.1-like layer half at 1 row with bf16 experts (hidden 5120, 256
-experts top-8, inter 2048, shared inter 2048). The 6-row Q8_0 workload is measured in the same
-run and reported under "rows6". Steps rotate over `--copies` independent weight copies and 64
+experts top-8, inter 2048, shared inter 2048). The 6-row Q8_0 and the 8-row MXFP4 (bf16 shared,
+one zero row) workloads are measured in the same run and reported under "rows6" and "rows8",
+and the chain of 8 bf16 layer halves (each taking the previous one's carry) under "chain8". Steps rotate over `--copies` independent weight copies and 64
 seeded input states, so routing changes every step and no weight is re-read from the 256 MB
 last-level cache; each step's algorithmic bytes count every distinct selected expert once.
 
@@ -117,6 +118,95 @@ class Workload:
         dur_ms = np.array([a.elapsed_time(b) for a, b in ev])
         span_ms = ev[0][0].elapsed_time(ev[-1][1])
         return dict(wall_s=wall, span_ms=span_ms, dur_ms=dur_ms, bytes=np.array(nbytes))
+
+
+class ChainWorkload:
+    """The 8-layer-half chain at 1 row: one step is 8 fused launches, layer l taking the carry of
+    layer l - 1 (its mix matvec skipped) and producing the next one's, the last with no carry.
+    Each layer's weights are distinct and resident (129 GB in all), so every launch streams its
+    own experts."""
+
+    def __init__(self, cfg):
+        import torch
+        import support
+        import moe_decode_layer_amd as mono
+        import synth.device as sdev
+        self.cfg = cfg
+        n = cfg.layers
+        t0 = time.time()
+        self.layers = [sdev.layer(cfg, l) for l in range(n)]
+        self.structs = [support.layer_struct(cfg, d) for d in self.layers]
+        self.states = [sdev.state(cfg, s) for s in range(64)]
+        self.shape = support.shape_of(cfg)
+        self.ws = torch.zeros(mono.mono_workspace_bytes(self.shape), dtype=torch.uint8,
+                              device="cuda")
+        mono.mono_workspace_init(self.ws, self.shape, support.stream())
+        ab = 4 if cfg.act == "f32" else 2
+        nb = cfg.rows * 4 * cfg.hidden * ab
+        self.bufs = [torch.zeros(nb, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        self.carry = [torch.zeros(cfg.rows * 25 * 4, dtype=torch.uint8, device="cuda")
+                      for _ in range(2)]
+        torch.cuda.synchronize()
+        log("  %s: %d layer halves resident in %.1f s" % (cfg.name, n, time.time() - t0))
+
+    def step(self, i: int, on_layer=None):
+        import moe_decode_layer_amd as mono
+        import support
+        n = self.cfg.layers
+        st = self.states[i % 64]
+        carry_in = None
+        for l in range(n):
+            nxt = self.layers[l + 1]["w_mix"] if l + 1 < n else None
+            out, cout = self.bufs[l % 2], self.carry[l % 2]
+            mono.mono_ffn_layer(self.shape, self.structs[l], nxt, st, carry_in, out,
+                                cout if nxt is not None else None, self.ws, support.stream())
+            if on_layer is not None:
+                on_layer(l)
+            st, carry_in = out, cout
+
+    def step_bytes(self, i: int) -> int:
+        """Algorithmic bytes of step i: per layer the distinct selected experts, the shared
+        expert, the router, bias and norm weight, W_mix of layer 0 (its own mix) and of every
+        next layer (the carry)."""
+        import torch
+        import moe_decode_layer_amd as mono
+        import support
+        import synth
+        c = self.cfg
+        per_routed = synth.expert_bytes(c.routed_fmt, c.inter, c.hidden)
+        per_shared = synth.expert_bytes(c.shared_fmt, c.shared_inter, c.hidden)
+        ab = 4 if c.act == "f32" else 2
+        w_mix = 24 * 4 * c.hidden * 4
+        total = [0]
+
+        def on_layer(l):
+            torch.cuda.synchronize()
+            idx = support.ws_tensor(self.shape, self.ws, mono.MONO_T_IDX, np.int32,
+                                    (c.rows, c.top_k))
+            b = len(np.unique(idx)) * per_routed + (per_shared if c.shared_inter else 0)
+            b += c.n_experts * c.hidden * 4 + c.n_experts * 4 + c.hidden * ab + 3 * 4 + 24 * 4
+            b += (w_mix if l == 0 else 0) + (w_mix if l + 1 < c.layers else 0)
+            total[0] += b
+
+        self.step(i, on_layer)
+        return total[0]
+
+    def run(self, steps: int, warmup: int):
+        import torch
+        nbytes = [self.step_bytes(i) for i in range(steps)]
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record()
+            self.step(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        dur_ms = np.array([a.elapsed_time(b) for a, b in ev])
+        span_ms = ev[0][0].elapsed_time(ev[-1][1])
+        return dict(span_ms=span_ms, dur_ms=dur_ms, bytes=np.array(nbytes))
 
 
 def summarize(res, cfg):
@@ -230,6 +320,28 @@ def pmc_summary(fetch_csv: str, write_csv: str):
     return out
 
 
+def trace_summary(trace_csv: str):
+    """Per-workload statistics of the layer kernel from a rocprofv3 --kernel-trace CSV.
+
+    The run builds its workloads one after another, each with weight fills and a workspace init
+    before its launches, so a maximal run of layer-kernel dispatches with no fill or init in
+    between is one workload (device copies of read-backs are ignored)."""
+    segs, cur = [], None
+    for r in _counter_rows(trace_csv):
+        name = r["Kernel_Name"]
+        if "k_ffn_layer" in name:
+            if cur is None or cur["name"] != name:
+                cur = dict(name=name, us=[], vgpr=r["VGPR_Count"], agpr=r["Accum_VGPR_Count"],
+                           sgpr=r["SGPR_Count"], lds=r["LDS_Block_Size"],
+                           scratch=r["Scratch_Size"], grid=r["Grid_Size_X"],
+                           wg=r["Workgroup_Size_X"])
+                segs.append(cur)
+            cur["us"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+        elif "synth_fill" in name or "k_ws_init" in name:
+            cur = None
+    return segs
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,12 +350,25 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="independent weight copies rotated")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-rows6", action="store_true")
+    ap.add_argument("--no-rows6", action="store_true", help="skip the 6- and 8-row workloads")
+    ap.add_argument("--no-chain", action="store_true", help="skip the 8-layer chain")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="summarise a rocprofv3 --kernel-trace CSV per workload and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc counter CSVs and exit (no GPU use)")
     args = ap.parse_args()
+    if args.trace_summary:
+        for sg in trace_summary(args.trace_summary):
+            us = np.array(sg["us"])
+            tail = us[-args.steps:]
+            print("%s\tdispatches=%d mean=%.1f median=%.1f min=%.1f max=%.1f last%d_mean=%.1f "
+                  "vgpr=%s agpr=%s sgpr=%s lds=%s scratch=%s grid=%sx%s" % (
+                      sg["name"], len(us), us.mean(), np.median(us), us.min(), us.max(),
+                      len(tail), tail.mean(), sg["vgpr"], sg["agpr"], sg["sgpr"], sg["lds"],
+                      sg["scratch"], int(sg["grid"]) // max(int(sg["wg"]), 1), sg["wg"]))
+        return
     if args.pmc_summary:
         for name, d in sorted(pmc_summary(*args.pmc_summary).items()):
             print("%s\t%s" % (name, "\t".join("%s=%.1f KiB x%d" % (c, v, n)
@@ -277,17 +402,34 @@ def main():
     log("  1 row:", json.dumps(r1))
     del w1
     torch.cuda.empty_cache()
-    rows6 = None
+    extra = {}
     if not args.no_rows6:
-        cfg6 = synth.CONFIGS[3]
-        w6 = Workload(cfg6, args.copies)
-        r6 = summarize(w6.run(args.steps, args.warmup), cfg6)
-        log("  6 rows:", json.dumps(r6))
-        rows6 = dict(workload=cfg6.name, rows=6, steps_per_s=r6["steps_per_s"],
-                     launch_us_median=r6["launch_us_median"], achieved_gbs=r6["achieved_gbs"],
-                     frac=r6["achieved_gbs"] / PEAK_HBM_GBS,
-                     bytes_per_step=r6["bytes_per_step_mean"])
-        del w6
+        for key, ci in (("rows6", 3), ("rows8", 4)):
+            cfgx = synth.CONFIGS[ci]
+            wx = Workload(cfgx, args.copies)
+            rx = summarize(wx.run(args.steps, args.warmup), cfgx)
+            log("  %s:" % key, json.dumps(rx))
+            extra[key] = dict(workload=cfgx.name, rows=cfgx.rows, steps_per_s=rx["steps_per_s"],
+                              launch_us_median=rx["launch_us_median"],
+                              launch_us_mean=rx["launch_us_mean"],
+                              achieved_gbs=rx["achieved_gbs"],
+                              frac=rx["achieved_gbs"] / PEAK_HBM_GBS,
+                              bytes_per_step=rx["bytes_per_step_mean"])
+            del wx
+            torch.cuda.empty_cache()
+    if not args.no_chain:
+        cfg5 = synth.CONFIGS[5]
+        wc = ChainWorkload(cfg5)
+        rc = summarize(wc.run(max(args.steps // 2, 1), args.warmup), cfg5)
+        log("  chain:", json.dumps(rc))
+        extra["chain8"] = dict(workload=cfg5.name, layer_halves=cfg5.layers,
+                               chain_steps_per_s=rc["steps_per_s"],
+                               chain_us_mean=rc["launch_us_mean"],
+                               us_per_layer_half=rc["launch_us_mean"] / cfg5.layers,
+                               achieved_gbs=rc["achieved_gbs"],
+                               frac=rc["achieved_gbs"] / PEAK_HBM_GBS,
+                               bytes_per_chain=rc["bytes_per_step_mean"])
+        del wc
         torch.cuda.empty_cache()
     cpu = None if args.no_cpu else cpu_baseline(cfg1, args.cpu_budget)
 
@@ -317,7 +459,7 @@ def main():
         "launch_us": {"median": r1["launch_us_median"], "p10": r1["launch_us_p10"],
                       "p90": r1["launch_us_p90"], "mean": r1["launch_us_mean"]},
         "bytes_per_step": r1["bytes_per_step_mean"],
-        "rows6": rows6,
+        **extra,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
