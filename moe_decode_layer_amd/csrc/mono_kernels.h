@@ -1830,9 +1830,38 @@ __device__ __forceinline__ void end_arrive(const Params& p, Smem& sm) {
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+/* When the new state overwrites the input (state_out == state), no workgroup may store its
+ * slice before every workgroup has read the whole input (mix partials and collapse): each
+ * workgroup publishes the launch tag in pre_done[wg] after its collapse, and the expand waits
+ * (bounded) until all of them carry it. Whole workgroup; returns false on expiry. */
+__device__ __forceinline__ bool wait_pre_done(const Params& p, Smem& sm, uint32_t tag) {
+  const int G = gridDim.x;
+  const __amdgpu_buffer_rsrc_t rs = coh_region(p.pre_done, (size_t)G * 8);
+  int ok = 1;
+  for (int w = threadIdx.x; w < G; w += kBlock) {
+    uint2 v = coh_b64(rs, (uint32_t)w * 8u);
+    if (v.x != tag) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (v.x != tag) {
+        __builtin_amdgcn_s_sleep(2);
+        v = coh_b64(rs, (uint32_t)w * 8u);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > sm.spin) {
+          ok = 0;
+          break;
+        }
+      }
+    }
+  }
+  const bool all = __syncthreads_and(ok) != 0;
+  if (!all && threadIdx.x == 0) report_timeout(p, PH_END);
+  return all;
+}
+
 template <int ACT, int RMAX, bool FUSED>
 __device__ __forceinline__ void ph_expand(const Params& p, Smem& sm, const float* blk) {
   const int tid = threadIdx.x;
+  if (FUSED && p.state_out == p.state && !wait_pre_done(p, sm, (uint32_t)(sm.epoch + 1)))
+    return;
   const Slice c = slice_of(p);
   const int h0 = c.h0, nh = c.nh;
   const int R = p.R, H = p.H, n = 4 * H;
@@ -2002,16 +2031,18 @@ __global__ void __launch_bounds__(kBlock) k_expand(Params p) {
   ph_expand<ACT, RMAX, false>(p, sm, blk);
 }
 
-/* The whole layer half in one persistent launch (one workgroup per compute unit):
- *   mix partials | arrive 1, load the pre-side parameters, wait 1 | pre side (every workgroup)
- *   | router rows | arrive 2, shared-expert gate/up, wait 2 | select + plan (every workgroup)
- *   | routed gate/up | arrive 3, issue the first down-projection loads and the expand's slice
- *   inputs, list the hidden rows to stage, wait 3 | down, block | expand + carry partials
- *   (workgroup q then sums carry output q over the grid once every partial carries this
- *   launch's tag).
+/* The whole layer half in one persistent launch (one workgroup per compute unit), with no grid
+ * barrier: every value one workgroup hands to another carries this launch's tag and the reader
+ * polls for it (bounded).
+ *   mix partials (tagged) | pre side in every workgroup (gathers the partials) | router parts
+ *   (tagged) beside Sinkhorn | select of every row (gathers the parts) while free waves claim
+ *   the shared expert's gate/up rows | plan | routed gate/up strided over the grid (tagged
+ *   hidden rows) | down in groups staged as their hidden rows arrive, block | expand + carry
+ *   partials (tagged; workgroup q sums carry output q over the grid).
  * Trace slots: 0 start, 1 mix partials, 2 pre-side inputs ready, 3 pre side, 4 router,
- * 5 shared gate/up, 6 router barrier passed, 7 select, 8 plan, 9 routed gate/up,
- * 10 gate/up barrier passed, 11 down + block, 12 expand, 13 carry. */
+ * 5 shared gate/up, 6 select rows, 7 select finished, 8 plan, 9 routed gate/up,
+ * 11 down + block, 12 expand, 13 carry; 14-18 inside the pre side, 19 select scores,
+ * 21 first down group staged, 22-24 router start, router dots, logits gathered. */
 template <int ACT, int RFMT, int SFMT, int RMAX>
 __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   __shared__ Smem sm;
@@ -2036,6 +2067,10 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   __syncthreads();
   stamp(p, tr, 2);
   if (!ph_hc_pre<ACT, RMAX>(p, sm, blockIdx.x == 0, true, tag)) return;
+  if (p.state_out == p.state) { /* in place: tell the expands this workgroup is done reading */
+    __syncthreads();
+    if (threadIdx.x == 0) st_coh(p.pre_done + blockIdx.x, (uint64_t)tag);
+  }
   stamp(p, tr, 3);
   /* router parts (waves 1 ..), then the select (waves 0 .. R - 1, polling the tagged logits),
    * then the shared expert's gate/up rows, claimed by whichever waves are free */

@@ -34,3 +34,24 @@ def test_fused_repeatable_across_interleaved_launches(name):
         else:
             support.assert_same(g.fused(b, 1, None, wn1), ref_b, keys)
     assert not np.array_equal(ref_a["new_state"], ref_b["new_state"])
+
+
+@pytest.mark.parametrize("name", ["tiny_f32_r1"] + list(CASES))
+def test_fused_in_place_equals_out_of_place(name):
+    """state_out == state_in: no workgroup may overwrite its slice of the state before every
+    workgroup has read all of it (the tiny case leaves most workgroups without expert work, so
+    they reach the expand first)."""
+    import torch
+    import support
+    cfg = synth.CONFIGS[1] if name == "tiny_f32_r1" else CASES[name]
+    g = support.Gpu(cfg, layers=(0, 1))
+    wn = g.layers[1]["w_mix"]
+    keys = ["idx", "weights", "block", "new_state", "carry", "norm"]
+    for sample in (0, 1, 2):
+        st = g.state(sample)
+        ref = g.fused(st, 0, None, wn)
+        inplace = st.clone()
+        got = g.fused(inplace, 0, None, wn, state_out=inplace)
+        support.assert_same(got, ref, keys)
+    del g
+    torch.cuda.empty_cache()
