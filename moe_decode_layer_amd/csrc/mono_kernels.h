@@ -279,20 +279,29 @@ __host__ __device__ constexpr size_t row_sbytes(int fmt, size_t k) {
   return fmt == Q8 ? (k / 32) * 2 : fmt == FP4 ? k / 32 : 0;
 }
 
-/* Loads step s of a row of K elements for this lane (zeros past the end of the row). */
+/* Buffer resource over one weight row (a wave-uniform address, so the resource lives in scalar
+ * registers): loads past `bytes` return zeros in hardware, so the weight loads need no bounds
+ * branch and a wave issues all of a chunk's loads before it waits for any. */
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* row, size_t bytes) {
+  /* readfirstlane returns int: go through uint32_t so the low word is not sign-extended */
+  const uint64_t a = reinterpret_cast<uint64_t>(row);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+/* Loads step s of a Q8_0 or MXFP4 row for this lane, with its block scale (zeros past the end
+ * of the row). */
 template <int FMT>
-__device__ __forceinline__ void wload(const uint8_t* vrow, const uint8_t* srow, int s, int lane,
-                                      int K, uint4& v, uint32_t& sc) {
+__device__ __forceinline__ void wload(__amdgpu_buffer_rsrc_t vr, __amdgpu_buffer_rsrc_t sr, int s,
+                                      int lane, uint4& v, uint32_t& sc) {
   const int q = s * 64 + lane;
-  const int k = q * Fmt<FMT>::EL;
-  if (k < K) {
-    v = *reinterpret_cast<const uint4*>(vrow + (size_t)q * 16);
-    if (FMT == Q8) sc = *reinterpret_cast<const uint16_t*>(srow + (k / 32) * 2);
-    if (FMT == FP4) sc = srow[k / 32];
-  } else {
-    v = make_uint4(0, 0, 0, 0);
-    sc = 0;
-  }
+  const v4u_t x = __builtin_amdgcn_raw_buffer_load_b128(vr, q * 16, 0, 0);
+  v = make_uint4(x[0], x[1], x[2], x[3]);
+  if (FMT == Q8) sc = __builtin_amdgcn_raw_buffer_load_b16(sr, (q * Fmt<FMT>::EL / 32) * 2, 0, 0);
+  else sc = __builtin_amdgcn_raw_buffer_load_b8(sr, q * Fmt<FMT>::EL / 32, 0, 0);
 }
 
 /* Exact decode of one 16-byte weight vector into packed bf16 pairs (element 2m in the low
@@ -379,20 +388,35 @@ struct WRegs {
 template <int FMT, int NR, int CH>
 __device__ __forceinline__ void wregs_load(WRegs<FMT, NR, CH>& W, const uint8_t* const (&vrow)[NR],
                                            const uint8_t* const (&srow)[NR], int K, int s0) {
-  constexpr int EL = Fmt<FMT>::EL;
   const int lane = threadIdx.x & 63;
-  const int nsteps = (K + 64 * EL - 1) / (64 * EL);
-#pragma unroll
-  for (int c = 0; c < CH; ++c)
+  if constexpr (FMT == Q8 || FMT == FP4) {
+    /* the decode would otherwise be sunk into a bounds branch per load, one load in flight */
+    const size_t vb = row_vbytes(FMT, K), sb = row_sbytes(FMT, K);
+    __amdgpu_buffer_rsrc_t vr[NR], sr[NR];
 #pragma unroll
     for (int m = 0; m < NR; ++m) {
-      if (s0 + c < nsteps) {
-        wload<FMT>(vrow[m], srow[m], s0 + c, lane, K, W.v[m][c], W.sc[m][c]);
-      } else {
-        W.v[m][c] = make_uint4(0, 0, 0, 0);
+      vr[m] = row_rsrc(vrow[m], vb);
+      sr[m] = row_rsrc(srow[m], sb);
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int m = 0; m < NR; ++m) wload<FMT>(vr[m], sr[m], s0 + c, lane, W.v[m][c], W.sc[m][c]);
+  } else {
+    constexpr int EL = Fmt<FMT>::EL;
+    const int nsteps = (K + 64 * EL - 1) / (64 * EL);
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        const int q = (s0 + c) * 64 + lane;
+        if (s0 + c < nsteps && q * EL < K)
+          W.v[m][c] = *reinterpret_cast<const uint4*>(vrow[m] + (size_t)q * 16);
+        else
+          W.v[m][c] = make_uint4(0, 0, 0, 0);
         W.sc[m][c] = 0;
       }
-    }
+  }
 }
 
 /* acc[m][r] += (chunk of row m) . act_r for every r in `mask` (per-lane partials); with one
