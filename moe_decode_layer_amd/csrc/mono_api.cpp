@@ -183,6 +183,7 @@ Params base_params(const mono_shape* s, const mono_layer* L, void* ws, int grid)
   p.mix_part = reinterpret_cast<uint64_t*>(b + W.mix_part);
   p.carry_part = reinterpret_cast<float*>(b + W.carry_part);
   p.pre_done = reinterpret_cast<uint64_t*>(b + W.pre_done);
+  p.y_part = reinterpret_cast<uint64_t*>(b + W.y_part);
   p.lgp = reinterpret_cast<uint64_t*>(b + W.lgp);
   p.trace = reinterpret_cast<uint64_t*>(b + W.trace);
   p.h_routed = b + W.h_routed;

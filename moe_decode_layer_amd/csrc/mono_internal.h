@@ -97,6 +97,7 @@ struct Params {
   uint64_t* mix_part; /* [nchunk][R][25] tagged mix partial sums: value bits | tag << 32 */
   float* carry_part; /* [R * 25][grid] tagged partials: value bits | epoch tag << 32 */
   uint64_t* pre_done; /* [grid] launch tag of each workgroup once it has read all of the state */
+  uint64_t* y_part;   /* [R][K + 1][H] tagged down-projection outputs (slot K: shared expert) */
   uint64_t* lgp;     /* [parts][R][E] tagged router logit parts (same format) */
   uint64_t* trace;   /* [grid][32] real-time stamps */
   size_t tag_words; /* u64 words from carry_part through lgp cleared by the workspace init */
@@ -105,7 +106,7 @@ struct Params {
 
 /* Workspace layout (byte offsets, 256-byte aligned regions). */
 struct WsLayout {
-  size_t ctl, mix_part, carry_part, pre_done, lgp, lgp_end, mixes, pre, post, comb, x, norm, logits, idx, weights,
+  size_t ctl, mix_part, carry_part, pre_done, y_part, lgp, lgp_end, mixes, pre, post, comb, x, norm, logits, idx, weights,
       h_routed, h_shared, shared, routed, block, carry, trace, total;
 };
 
@@ -140,6 +141,7 @@ inline WsLayout ws_layout(const mono_shape& s) {
   L.ctl = take(CTL_WORDS * 4);
   L.carry_part = take((size_t)kMaxGrid * R * kNCarry * 8);
   L.pre_done = take((size_t)kMaxGrid * 8);
+  L.y_part = take(R * (k + 1) * H * 8);
   L.mix_part = take(nchunk * R * kNCarry * 8);
   L.lgp = take(router_parts(s.hidden) * R * E * 8);
   /* hidden rows, tagged: each value with the launch tag beside it (bf16 | tag16 << 16 in a

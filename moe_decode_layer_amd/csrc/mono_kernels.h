@@ -305,8 +305,8 @@ __device__ __forceinline__ void wload(__amdgpu_buffer_rsrc_t vr, __amdgpu_buffer
 }
 
 /* Exact decode of one 16-byte weight vector into packed bf16 pairs (element 2m in the low
- * half of pair m) and its block scale. Q8_0: each int8 q becomes f32 through the unsigned byte
- * q ^ 0x80 minus 128, whose top 16 bits are the exact bf16 of q. MXFP4: each byte converts to
+ * half of pair m) and its block scale. Q8_0: each int8 q converts to f32 exactly, and the top 16
+ * bits of that f32 are the exact bf16 of q (|q| <= 128 needs 8 significant bits). MXFP4: each byte converts to
  * a bf16 pair (low nibble first) with unit scale; the e8m0 scale multiplies the partial sum. */
 template <int FMT>
 __device__ __forceinline__ void decode(const uint4& v, uint32_t sc, uint32_t (&w)[Fmt<FMT>::PAIRS],
@@ -315,14 +315,14 @@ __device__ __forceinline__ void decode(const uint4& v, uint32_t sc, uint32_t (&w
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
     scale = 1.0f;
   } else if constexpr (FMT == Q8) {
-    const uint32_t d[4] = {v.x ^ 0x80808080u, v.y ^ 0x80808080u, v.z ^ 0x80808080u,
-                           v.w ^ 0x80808080u};
+    /* one sign-extending byte-to-float conversion per value */
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float f0 = (float)(d[i] & 0xFFu) - 128.0f;
-      const float f1 = (float)((d[i] >> 8) & 0xFFu) - 128.0f;
-      const float f2 = (float)((d[i] >> 16) & 0xFFu) - 128.0f;
-      const float f3 = (float)(d[i] >> 24) - 128.0f;
+      const float f0 = (float)(int)(int8_t)d[i];
+      const float f1 = (float)(int)(int8_t)(d[i] >> 8);
+      const float f2 = (float)(int)(int8_t)(d[i] >> 16);
+      const float f3 = (float)(int)(int8_t)(d[i] >> 24);
       w[2 * i] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
       w[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
     }
@@ -496,6 +496,8 @@ struct Smem {
   int nv;
   int sel_ok;      /* cleared when a select wave's logits did not arrive */
   int shared_next; /* next shared-expert gate/up task of this workgroup (fused launch) */
+  int routed_next; /* next routed gate/up task of this workgroup (fused launch) */
+  int down_next;   /* next down quad of the current staged group (fused launch, several rows) */
   int nU;
   int flag;
   uint64_t epoch;
@@ -1344,16 +1346,47 @@ __device__ __forceinline__ void ph_plan(const Params& p, Smem& sm) {
  * before SwiGLU and the product after it]. Task (expert, intermediate row i): one wave streams
  * gate row i and up row i once and applies them to every row that chose the expert.
  * READING: routed experts use the shared expert's rounding points. */
+/* Gate row i and up row i of expert e (and their scale rows). */
+template <int FMT>
+__device__ __forceinline__ void gu_rows(const Params& p, const Mat& m, int e, int i, int inter,
+                                        const uint8_t* (&vr)[2], const uint8_t* (&sr)[2]) {
+  const size_t vb = row_vbytes(FMT, p.H), sb = row_sbytes(FMT, p.H);
+  const size_t row = (size_t)e * inter + i;
+  vr[0] = m.gate + row * vb;
+  vr[1] = m.up + row * vb;
+  sr[0] = m.gate_s ? m.gate_s + row * sb : nullptr;
+  sr[1] = m.up_s ? m.up_s + row * sb : nullptr;
+}
+
+/* SwiGLU of hidden row i from the per-lane partial sums of gate (acc[0]) and up (acc[1]). */
+template <int ACT, int RMAX>
+__device__ __forceinline__ void gu_store(const Params& p, const Smem& sm, float (&acc)[2][RMAX],
+                                         int i, uint32_t mask, int u, bool is_shared,
+                                         uint32_t htag, bool hskip) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    if (!(mask & (1u << r))) continue;
+    const float g = act_round<ACT>(wave_sum(acc[0][r]));
+    const float uu = act_round<ACT>(wave_sum(acc[1][r]));
+    const float h = act_round<ACT>(g / (1.0f + expf(-g)) * uu);
+    if (lane == 0 && !hskip) {
+      if (is_shared)
+        hid_store<ACT>(p.h_shared, (size_t)r * p.Is + i, h, htag);
+      else
+        hid_store<ACT>(p.h_routed, ((size_t)r * p.K + sm.uslot[u][r]) * p.I + i, h, htag);
+    }
+  }
+}
+
 template <int ACT, int FMT, int RMAX>
 __device__ __forceinline__ void gateup_task(const Params& p, const Smem& sm, const Mat& m,
                                             int e, int i, int inter, uint32_t mask, int u,
                                             bool is_shared, uint32_t htag, bool hskip) {
   const int H = p.H, lane = threadIdx.x & 63;
-  const size_t vb = row_vbytes(FMT, H), sb = row_sbytes(FMT, H);
-  const size_t row = (size_t)e * inter + i;
-  const uint8_t* vr[2] = {m.gate + row * vb, m.up + row * vb};
-  const uint8_t* sr[2] = {m.gate_s ? m.gate_s + row * sb : nullptr,
-                          m.up_s ? m.up_s + row * sb : nullptr};
+  const uint8_t* vr[2];
+  const uint8_t* sr[2];
+  gu_rows<FMT>(p, m, e, i, inter, vr, sr);
   const void* arow[RMAX];
   act_rows_ptrs<ACT, RMAX>(p, sm, arow);
   float acc[2][RMAX];
@@ -1385,6 +1418,18 @@ __device__ __forceinline__ void ph_gateup_shared(const Params& p, const Smem& sm
     gateup_task<ACT, SFMT, RMAX>(p, sm, p.shared, 0, i, p.Is, mask, 0, true, 0u, false);
 }
 
+/* A value the whole wave holds alike, moved to a scalar register, so that branches on it are
+ * scalar branches rather than per-lane masks. */
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+/* Next task index of this wave from an LDS counter: all 64 lanes add 1 and lane 0's old value
+ * (a multiple of 64) is read back uniformly, so there is no divergent branch in the loop. */
+__device__ __forceinline__ int claim(int* counter) {
+  return __builtin_amdgcn_readfirstlane(atomicAdd(counter, 1)) / 64;
+}
+
 /* Shared-expert gate/up in the fused launch: workgroup g owns rows g, g + grid, ...; its waves
  * claim them one at a time from an LDS counter (sm.shared_next, zeroed beforehand), so a wave
  * that also selects joins when it is done. */
@@ -1394,26 +1439,55 @@ __device__ __forceinline__ void ph_gateup_shared_claim(const Params& p, Smem& sm
   if (p.Is <= 0) return;
   const uint32_t mask = (1u << p.R) - 1u;
   for (;;) {
-    /* all 64 lanes add 1 and lane 0's old value (a multiple of 64) is read back uniformly: no
-     * divergent branch in the loop, so every lane stays in the same iteration and they leave
-     * together */
-    const int n = __builtin_amdgcn_readfirstlane(atomicAdd(&sm.shared_next, 1)) / 64;
-    const int i = (int)blockIdx.x + n * (int)gridDim.x;
+    const int i = (int)blockIdx.x + claim(&sm.shared_next) * (int)gridDim.x;
     if (i >= p.Is) break;
     gateup_task<ACT, SFMT, RMAX>(p, sm, p.shared, 0, i, p.Is, mask, 0, true, htag, hskip);
   }
 }
 
-/* Routed gate/up: task t of the nU * I tasks goes to wave t % waves of the grid, spread over
- * compute units first, so that at any moment the grid streams one contiguous stretch of rows. */
+/* Routed gate/up: workgroup b owns tasks b, b + grid, ... of the nU * I tasks (expert-major),
+ * so at any moment the grid streams one contiguous stretch of rows; its waves claim them one at
+ * a time, so a wave that runs ahead takes more and the workgroup's waves end together. At
+ * several rows, when a row fits one chunk, a wave issues the loads of its next task before it
+ * computes the current one. */
 template <int ACT, int RFMT, int RMAX>
-__device__ __forceinline__ void ph_gateup_routed(const Params& p, const Smem& sm, uint32_t htag,
+__device__ __forceinline__ void ph_gateup_routed(const Params& p, Smem& sm, uint32_t htag,
                                                  bool hskip) {
-  const long T = (long)sm.nU * p.I;
-  const long nwt = (long)gridDim.x * kWaves;
-  for (long t = wave_major_id(); t < T; t += nwt) {
-    const int u = (int)(t / p.I), i = (int)(t % p.I);
-    gateup_task<ACT, RFMT, RMAX>(p, sm, p.routed, sm.U[u], i, p.I, sm.umask[u], u, false, htag,
+  const int T = sm.nU * p.I;
+  constexpr int CH = Fmt<RFMT>::CH_GU;
+  auto next = [&]() -> int { return (int)blockIdx.x + claim(&sm.routed_next) * (int)gridDim.x; };
+  if constexpr (RMAX > 1) {
+    if (p.H <= 64 * Fmt<RFMT>::EL * CH) {
+      const void* arow[RMAX];
+      act_rows_ptrs<ACT, RMAX>(p, sm, arow);
+      auto load = [&](WRegs<RFMT, 2, CH>& W, int t) {
+        const uint8_t* vr[2];
+        const uint8_t* sr[2];
+        gu_rows<RFMT>(p, p.routed, sm.U[t / p.I], t % p.I, p.I, vr, sr);
+        wregs_load(W, vr, sr, p.H, 0);
+      };
+      WRegs<RFMT, 2, CH> A, B;
+      int t = next();
+      if (t < T) load(A, t);
+      while (t < T) {
+        const int tn = next();
+        if (tn < T) load(B, tn);
+        const int u = t / p.I;
+        const uint32_t mask = uniform(sm.umask[u]);
+        float acc[2][RMAX];
+#pragma unroll
+        for (int r = 0; r < RMAX; ++r) acc[0][r] = acc[1][r] = 0.0f;
+        wregs_dot<RFMT, ACT, RMAX, 2, CH>(A, p.H, 0, arow, mask, acc);
+        gu_store<ACT, RMAX>(p, sm, acc, t % p.I, mask, u, false, htag, hskip);
+        t = tn;
+        A = B;
+      }
+      return;
+    }
+  }
+  for (int t = next(); t < T; t = next()) {
+    const int u = t / p.I, i = t % p.I;
+    gateup_task<ACT, RFMT, RMAX>(p, sm, p.routed, sm.U[u], i, p.I, uniform(sm.umask[u]), u, false, htag,
                                  hskip);
   }
 }
@@ -1468,7 +1542,7 @@ __device__ __forceinline__ void down_task(const Params& p, const Smem& sm, const
   const uint8_t* vr[kRG];
   const uint8_t* sr[kRG];
   down_rows<ACT, FMT>(p, g, m, e, inter, q, vr, sr);
-  const uint32_t mask = sm.umask[item];
+  const uint32_t mask = uniform(sm.umask[item]);
   const void* arow[RMAX];
 #pragma unroll
   for (int r = 0; r < RMAX; ++r)
@@ -1796,6 +1870,169 @@ __device__ __forceinline__ bool ph_down(const Params& p, Smem& sm, uint32_t htag
 }
 
 /* ------------------------------------------------------------------------------------------
+ * Down phase of the fused launch at several rows. The shared expert is used by every row, so
+ * its down rows cost R dot products per weight: each workgroup takes the shared rows of its own
+ * hidden-position slice, as the per-slice down phase does. The routed down rows of all
+ * distinct experts form one list of (expert, kRG consecutive output rows) quads, and workgroup
+ * w takes an equal contiguous stretch of it, so a workgroup stages in LDS only the hidden rows
+ * of the one or two experts its stretch touches (polling their tags) instead of all of them.
+ * Every output y[h][r][slot] is published tagged; each workgroup then gathers the y values of
+ * its slice and forms routed, shared and block as the per-slice down phase does. Each y value
+ * comes from the same per-quad dot product as there, so the results are the same bits. */
+
+/* One quad: down rows hb .. hb + nr - 1 (nr <= kRG; the rest repeat the last row and are not
+ * stored) of item `item` against its staged hidden rows; publishes y[h][r][slot]
+ * (value bits | tag << 32) for every row r that uses the item. */
+template <int ACT, int FMT, int RMAX>
+__device__ __forceinline__ void em_down_task(const Params& p, const Smem& sm, const Mat& m, int e,
+                                             int inter, int item, int hb, int nr, bool is_shared,
+                                             int Kp, uint32_t tag) {
+  const int lane = threadIdx.x & 63;
+  constexpr int CH = Fmt<FMT>::CH_DN;
+  const size_t vb = row_vbytes(FMT, inter), sb = row_sbytes(FMT, inter);
+  const uint8_t* vr[kRG];
+  const uint8_t* sr[kRG];
+#pragma unroll
+  for (int c = 0; c < kRG; ++c) {
+    const size_t row = (size_t)e * p.H + hb + (c < nr ? c : nr - 1);
+    vr[c] = m.down + row * vb;
+    sr[c] = m.down_s ? m.down_s + row * sb : nullptr;
+  }
+  const uint32_t mask = uniform(sm.umask[item]);
+  const void* arow[RMAX];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r)
+    arow[r] = sm.big + (size_t)((mask & (1u << r)) ? sm.voff[item][r] : 0) * 16;
+  float acc[kRG][RMAX];
+#pragma unroll
+  for (int c = 0; c < kRG; ++c)
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) acc[c][r] = 0.0f;
+  dot_rows<FMT, ACT, RMAX, kRG, CH>(vr, sr, inter, arow, mask, acc);
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    if (!(mask & (1u << r))) continue;
+    const int slot = is_shared ? p.K : sm.uslot[item][r];
+#pragma unroll
+    for (int c = 0; c < kRG; ++c) {
+      const float t = wave_sum(acc[c][r]);
+      if (lane == c && c < nr)
+        st_coh(p.y_part + ((size_t)(hb + c) * p.R + r) * Kp + slot,
+               ((uint64_t)tag << 32) | __float_as_uint(t));
+    }
+  }
+}
+
+/* Gathers the tagged y values of the slice, [nh][R][Kp], into LDS at dst as floats, polling
+ * (bounded) until each carries `tag`. Whole workgroup; returns false (uniform) on expiry. */
+__device__ __forceinline__ bool em_gather_y(const Params& p, Smem& sm, int h0, int nh, int Kp,
+                                            float* dst, uint32_t tag) {
+  const int tid = threadIdx.x;
+  const int n = nh * p.R * Kp;
+  const __amdgpu_buffer_rsrc_t yr =
+      coh_region(p.y_part + (size_t)h0 * p.R * Kp, (size_t)(n > 0 ? n : 1) * 8);
+  int ok = 1;
+  constexpr int B = 4;
+  for (int v0 = 0; v0 < n; v0 += B * kBlock) {
+    uint2 b[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const int v = v0 + k * kBlock + tid;
+      if (v < n) b[k] = coh_b64(yr, (uint32_t)v * 8u);
+    }
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const int v = v0 + k * kBlock + tid;
+      if (v >= n) continue;
+      if (b[k].y != tag) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (b[k].y != tag) {
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_sleep(1);
+          b[k] = coh_b64(yr, (uint32_t)v * 8u);
+          if (__builtin_amdgcn_s_memrealtime() - t0 > sm.spin) {
+            ok = 0;
+            break;
+          }
+        }
+      }
+      dst[v] = __uint_as_float(b[k].x);
+    }
+  }
+  const bool all = __syncthreads_and(ok) != 0;
+  if (!all && tid == 0) report_timeout(p, PH_GATEUP);
+  return all;
+}
+
+template <int ACT, int RFMT, int SFMT, int RMAX>
+__device__ __forceinline__ bool ph_down_em(const Params& p, Smem& sm, uint32_t htag) {
+  const int tid = threadIdx.x, wave = tid >> 6, R = p.R;
+  const uint32_t tag = (uint32_t)(sm.epoch + 1);
+  const int nU = sm.nU, Kp = p.K + (p.Is > 0 ? 1 : 0), off = p.Is > 0 ? 1 : 0;
+  const size_t ab = ACT == F32 ? 4 : 2;
+  const int nqi = p.H / kRG;
+  const Slice c = slice_of(p);
+  SliceRegs sreg;
+  slice_prefetch<ACT>(p, c, sreg);
+  bool first = true;
+  /* the shared expert's down rows of this workgroup's slice (its hidden rows are complete
+   * since before the select) */
+  if (p.Is > 0 && c.nh > 0) {
+    stage_list(p, sm, 0, 1, ab);
+    if (!stage_copy<ACT>(p, sm, true, htag)) return false;
+    slice_store(p, c, sm, sreg);
+    stamp(p, sm.trace_on != 0, 21);
+    first = false;
+    for (int t = wave; t * kRG < c.nh; t += kWaves) {
+      const int nr = c.nh - t * kRG < kRG ? c.nh - t * kRG : kRG;
+      em_down_task<ACT, SFMT, RMAX>(p, sm, p.shared, 0, p.Is, nU, c.h0 + t * kRG, nr, true, Kp,
+                                    tag);
+    }
+  }
+  /* this workgroup's stretch of routed quads */
+  const long QR = (long)nU * nqi;
+  const int q0 = (int)(QR * blockIdx.x / gridDim.x), q1 = (int)(QR * (blockIdx.x + 1) / gridDim.x);
+  int u = q0 / nqi;
+  const int uend = q1 > q0 ? (q1 - 1) / nqi + 1 : u;
+  while (u < uend) {
+    const int u1 = down_group_end(p, sm, u + off, ab, uend - u) - off;
+    if (!first) __syncthreads(); /* the previous items' tasks are done with the staging area */
+    stage_list(p, sm, u + off, u1 + off, ab);
+    if (!stage_copy<ACT>(p, sm, true, htag)) return false;
+    if (first) {
+      slice_store(p, c, sm, sreg);
+      stamp(p, sm.trace_on != 0, 21);
+      first = false;
+    }
+    const int qa = q0 > u * nqi ? q0 : u * nqi, qb = q1 < u1 * nqi ? q1 : u1 * nqi;
+    for (int q = qa + wave; q < qb; q += kWaves) {
+      const int it = q / nqi;
+      em_down_task<ACT, RFMT, RMAX>(p, sm, p.routed, sm.U[it], p.I, it, (q % nqi) * kRG, kRG,
+                                    false, Kp, tag);
+    }
+    u = u1;
+  }
+  if (first) slice_store(p, c, sm, sreg);
+  const DownGeo g = down_geo(p, sm);
+  if (!em_gather_y(p, sm, g.h0, g.nh, Kp, g.y, tag)) return false;
+  for (int q = tid; q < g.nh * R; q += kBlock) {
+    const int hl = q / R, r = q % R;
+    const float* y = g.y + ((size_t)hl * R + r) * Kp;
+    float routed = 0.0f;
+    for (int j = 0; j < p.K; ++j) routed = fmaf(sm.sel_w[r][j], y[j], routed);
+    const float shared = p.Is > 0 ? act_round<ACT>(y[p.K]) : 0.0f;
+    const float blk = act_round<ACT>(routed + shared);
+    const size_t o = (size_t)r * p.H + g.h0 + hl;
+    if (p.routed_out) p.routed_out[o] = routed;
+    if (p.shared_out) act_st<ACT>(p.shared_out, o, shared);
+    if (p.block) act_st<ACT>(p.block, o, blk);
+    g.blk[q] = blk;
+  }
+  __syncthreads();
+  return true;
+}
+
+/* ------------------------------------------------------------------------------------------
  * Phase: expand + carry for the workgroup's slice [ds4 HC fusion commit: post/comb expand +
  * BF16; SGLang fused post/pre page: bf16 residual materialisation + next pre-norm GEMM
  * partials + RMS square-sum partials]. new[i][h] = bf16(post_i block[h] + sum_j comb[i][j]
@@ -2013,7 +2250,10 @@ __global__ void __launch_bounds__(kBlock) k_select(Params p) {
 template <int ACT, int RFMT, int SFMT, int RMAX>
 __global__ void __launch_bounds__(kBlock) k_gateup(Params p) {
   __shared__ Smem sm;
-  if (threadIdx.x == 0) sm.trace_on = 0;
+  if (threadIdx.x == 0) {
+    sm.trace_on = 0;
+    sm.routed_next = 0; /* read after ph_plan's barrier */
+  }
   load_act_rows<ACT>(p.norm_in, p.R, p.H, sm);
   load_selection(p, sm);
   ph_plan(p, sm);
@@ -2087,6 +2327,7 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   if (threadIdx.x == 0) {
     sm.sel_ok = 1;
     sm.shared_next = 0;
+    sm.routed_next = 0;
   }
   __syncthreads();
   stamp(p, tr, 2);
@@ -2115,7 +2356,15 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   stamp(p, tr, 8);
   ph_gateup_routed<ACT, RFMT, RMAX>(p, sm, htag, hskip);
   stamp(p, tr, 9);
-  if (!ph_down<ACT, RFMT, SFMT, RMAX, true>(p, sm, htag)) return;
+  /* end of each other wave's gate/up rows: slots 25 .. 31 */
+  if (tr && (threadIdx.x & 63) == 0 && threadIdx.x > 0)
+    p.trace[(size_t)blockIdx.x * kTraceSlots + 24 + (threadIdx.x >> 6)] =
+        __builtin_amdgcn_s_memrealtime();
+  if constexpr (RMAX > 1) {
+    if (!ph_down_em<ACT, RFMT, SFMT, RMAX>(p, sm, htag)) return;
+  } else {
+    if (!ph_down<ACT, RFMT, SFMT, RMAX, true>(p, sm, htag)) return;
+  }
   stamp(p, tr, 11);
   const DownGeo g = down_geo(p, sm);
   ph_expand<ACT, RMAX, true>(p, sm, g.blk);

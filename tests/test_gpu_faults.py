@@ -13,23 +13,28 @@ pytestmark = pytest.mark.gpu
 
 PH_MIX, PH_ROUTER, PH_GATEUP = 1, 2, 3
 SMALL = synth.CONFIGS[2].with_(hidden=512, n_experts=32, top_k=4, inter=256, shared_inter=256)
+# several rows take the multi-row down phase (expert-row stretches, tagged outputs)
+SMALL_R3 = synth.CONFIGS[3].with_(rows=3, hidden=512, n_experts=32, top_k=4, inter=256,
+                                  shared_inter=256)
 
 
+@pytest.mark.parametrize("rows", [1, 3])
 @pytest.mark.parametrize("phase", [PH_MIX, PH_ROUTER, PH_GATEUP])
-def test_withheld_values_time_out_and_recover(phase):
+def test_withheld_values_time_out_and_recover(phase, rows):
     import torch
     import support
     import moe_decode_layer_amd as mono
-    print("values withheld at point", phase, flush=True)
-    g = support.Gpu(SMALL, layers=(0, 1))
+    print("values withheld at point", phase, "rows", rows, flush=True)
+    cfg = SMALL if rows == 1 else SMALL_R3
+    g = support.Gpu(cfg, layers=(0, 1))
     st = g.state(0)
     wn = g.layers[1]["w_mix"]
     ref = g.fused(st, 0, None, wn)
     grid = mono.mono_grid_size()
     # 2 ms limit (100 MHz counter); workgroup 0 (it has mix, router and gate/up work) withholds
     mono.mono_workspace_set_debug(g.ws, 200000, 0, phase, support.stream())
-    new = g.buf(SMALL.rows * 4 * SMALL.hidden * 2)
-    carry = g.buf(SMALL.rows * 25 * 4)
+    new = g.buf(cfg.rows * 4 * cfg.hidden * 2)
+    carry = g.buf(cfg.rows * 25 * 4)
     mono.mono_ffn_layer(g.shape, g.structs[0], wn, st, None, new, carry, g.ws, support.stream())
     status, err = mono.mono_workspace_poll(g.ws, support.stream())
     assert status == mono.MONO_E_TIMEOUT
