@@ -142,9 +142,11 @@ mono_status mono_workspace_set_debug(void* ws, uint32_t spin_limit_ticks, int32_
 /* Test hook: when enable != 0, later mono_ffn_layer launches on this workspace record, per
  * workgroup, the 100 MHz real-time counter at phase boundaries (MONO_T_TRACE): 0 start,
  * 1 mix partials, 2 pre-side inputs ready, 3 pre side, 4 router, 5 shared gate/up, 6 select
- * rows, 7 select finished, 8 plan, 9 routed gate/up, 11 down + block, 12 expand, 13 carry;
+ * rows, 7 select finished, 8 plan, 9 routed gate/up, 10 routed down (several rows), 11 down +
+ * block, 12 expand, 13 carry;
  * 14-18 inside the pre side (raw sums, mixes, gates, collapse, sum of squares), 19 select
- * scores, 21 first down group staged, 22 router start, 23 router dots, 24 logits gathered,
+ * scores, 20 shared down (several rows), 21 first down group staged, 22 router start,
+ * 23 router dots, 24 logits gathered,
  * 25-31 routed gate/up done in waves 1-7 (slot 9 is wave 0).
  * Enqueued on `stream`. */
 mono_status mono_workspace_set_trace(void* ws, int enable, void* stream);

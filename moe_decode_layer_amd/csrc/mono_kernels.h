@@ -271,6 +271,14 @@ template <> struct Fmt<F32> { static constexpr int EL = 4, CH_GU = 8, CH_DN = 4,
 template <> struct Fmt<BF16> { static constexpr int EL = 8, CH_GU = 10, CH_DN = 4, PAIRS = 4; };
 template <> struct Fmt<Q8> { static constexpr int EL = 16, CH_GU = 5, CH_DN = 2, PAIRS = 8; };
 template <> struct Fmt<FP4> { static constexpr int EL = 32, CH_GU = 3, CH_DN = 1, PAIRS = 16; };
+/* Routed tasks of the fused launch at several rows when the expert serves one row (the common
+ * case): GB hidden rows per gate/up task and DG down rows per down task, so that a wave keeps
+ * 16-20 KB of weights in flight whatever the format. */
+template <int FMT> struct Wide;
+template <> struct Wide<F32> { static constexpr int GB = 1, DG = 4; };
+template <> struct Wide<BF16> { static constexpr int GB = 1, DG = 4; };
+template <> struct Wide<Q8> { static constexpr int GB = 2, DG = 8; };
+template <> struct Wide<FP4> { static constexpr int GB = 4, DG = 16; };
 
 __host__ __device__ constexpr size_t row_vbytes(int fmt, size_t k) {
   return fmt == F32 ? 4 * k : fmt == BF16 ? 2 * k : fmt == Q8 ? k : k / 2;
@@ -497,7 +505,7 @@ struct Smem {
   int sel_ok;      /* cleared when a select wave's logits did not arrive */
   int shared_next; /* next shared-expert gate/up task of this workgroup (fused launch) */
   int routed_next; /* next routed gate/up task of this workgroup (fused launch) */
-  int down_next;   /* next down quad of the current staged group (fused launch, several rows) */
+  int down_next;   /* next down block of the current staged group (fused launch, several rows) */
   int nU;
   int flag;
   uint64_t epoch;
@@ -1383,7 +1391,7 @@ template <int ACT, int FMT, int RMAX>
 __device__ __forceinline__ void gateup_task(const Params& p, const Smem& sm, const Mat& m,
                                             int e, int i, int inter, uint32_t mask, int u,
                                             bool is_shared, uint32_t htag, bool hskip) {
-  const int H = p.H, lane = threadIdx.x & 63;
+  const int H = p.H;
   const uint8_t* vr[2];
   const uint8_t* sr[2];
   gu_rows<FMT>(p, m, e, i, inter, vr, sr);
@@ -1393,19 +1401,7 @@ __device__ __forceinline__ void gateup_task(const Params& p, const Smem& sm, con
 #pragma unroll
   for (int r = 0; r < RMAX; ++r) acc[0][r] = acc[1][r] = 0.0f;
   dot_rows<FMT, ACT, RMAX, 2, Fmt<FMT>::CH_GU>(vr, sr, H, arow, mask, acc);
-#pragma unroll
-  for (int r = 0; r < RMAX; ++r) {
-    if (!(mask & (1u << r))) continue;
-    const float g = act_round<ACT>(wave_sum(acc[0][r]));
-    const float uu = act_round<ACT>(wave_sum(acc[1][r]));
-    const float h = act_round<ACT>(g / (1.0f + expf(-g)) * uu);
-    if (lane == 0 && !hskip) {
-      if (is_shared)
-        hid_store<ACT>(p.h_shared, (size_t)r * p.Is + i, h, htag);
-      else
-        hid_store<ACT>(p.h_routed, ((size_t)r * p.K + sm.uslot[u][r]) * p.I + i, h, htag);
-    }
-  }
+  gu_store<ACT, RMAX>(p, sm, acc, i, mask, u, is_shared, htag, hskip);
 }
 
 /* Shared-expert gate/up: Is tasks spread over compute units first. */
@@ -1445,50 +1441,79 @@ __device__ __forceinline__ void ph_gateup_shared_claim(const Params& p, Smem& sm
   }
 }
 
-/* Routed gate/up: workgroup b owns tasks b, b + grid, ... of the nU * I tasks (expert-major),
- * so at any moment the grid streams one contiguous stretch of rows; its waves claim them one at
- * a time, so a wave that runs ahead takes more and the workgroup's waves end together. At
- * several rows, when a row fits one chunk, a wave issues the loads of its next task before it
- * computes the current one. */
+/* GB consecutive hidden rows i0 .. of routed expert u for the NA rows in `mask` (NA = its
+ * population): the 2 GB gate and up weight rows stream at once. */
+template <int ACT, int FMT, int NA, int GB>
+__device__ __forceinline__ void gu_wide(const Params& p, const Smem& sm, int u, int i0,
+                                        uint32_t mask, uint32_t htag, bool hskip) {
+  const int lane = threadIdx.x & 63;
+  int rows[NA];
+  uint32_t m = mask;
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    rows[a] = __builtin_ctz(m);
+    m &= m - 1u;
+  }
+  const uint8_t* vr[2 * GB];
+  const uint8_t* sr[2 * GB];
+#pragma unroll
+  for (int g = 0; g < GB; ++g) {
+    const uint8_t* v2[2];
+    const uint8_t* s2[2];
+    gu_rows<FMT>(p, p.routed, sm.U[u], i0 + g, p.I, v2, s2);
+    vr[2 * g] = v2[0];
+    vr[2 * g + 1] = v2[1];
+    sr[2 * g] = s2[0];
+    sr[2 * g + 1] = s2[1];
+  }
+  const void* arow[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) arow[a] = sm.big + (size_t)rows[a] * p.H * (ACT == F32 ? 4 : 2);
+  float acc[2 * GB][NA];
+#pragma unroll
+  for (int k = 0; k < 2 * GB; ++k)
+#pragma unroll
+    for (int a = 0; a < NA; ++a) acc[k][a] = 0.0f;
+  dot_rows<FMT, ACT, NA, 2 * GB, Fmt<FMT>::CH_GU>(vr, sr, p.H, arow, (1u << NA) - 1u, acc);
+#pragma unroll
+  for (int g = 0; g < GB; ++g)
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+      const int r = rows[a];
+      const float gg = act_round<ACT>(wave_sum(acc[2 * g][a]));
+      const float uu = act_round<ACT>(wave_sum(acc[2 * g + 1][a]));
+      const float h = act_round<ACT>(gg / (1.0f + expf(-gg)) * uu);
+      if (lane == 0 && !hskip)
+        hid_store<ACT>(p.h_routed, ((size_t)r * p.K + sm.uslot[u][r]) * p.I + i0 + g, h, htag);
+    }
+}
+
+/* Routed gate/up: workgroup b owns tasks b, b + grid, ... (expert-major order), so at any
+ * moment the grid streams one contiguous stretch of rows; its waves claim them one at a time, so
+ * a wave that runs ahead takes more and the workgroup's waves end together. At several rows a
+ * task is GB consecutive hidden rows of one expert: when one or two rows use the expert, all
+ * 2 GB weight rows stream at once against them; otherwise the rows go one by one for every row
+ * that uses the expert. Every hidden value comes from the same per-row dot product either way. */
 template <int ACT, int RFMT, int RMAX>
 __device__ __forceinline__ void ph_gateup_routed(const Params& p, Smem& sm, uint32_t htag,
                                                  bool hskip) {
-  const int T = sm.nU * p.I;
-  constexpr int CH = Fmt<RFMT>::CH_GU;
+  constexpr int GB = RMAX > 1 ? Wide<RFMT>::GB : 1;
+  const int nb = p.I / GB;
+  const int T = sm.nU * nb;
   auto next = [&]() -> int { return (int)blockIdx.x + claim(&sm.routed_next) * (int)gridDim.x; };
-  if constexpr (RMAX > 1) {
-    if (p.H <= 64 * Fmt<RFMT>::EL * CH) {
-      const void* arow[RMAX];
-      act_rows_ptrs<ACT, RMAX>(p, sm, arow);
-      auto load = [&](WRegs<RFMT, 2, CH>& W, int t) {
-        const uint8_t* vr[2];
-        const uint8_t* sr[2];
-        gu_rows<RFMT>(p, p.routed, sm.U[t / p.I], t % p.I, p.I, vr, sr);
-        wregs_load(W, vr, sr, p.H, 0);
-      };
-      WRegs<RFMT, 2, CH> A, B;
-      int t = next();
-      if (t < T) load(A, t);
-      while (t < T) {
-        const int tn = next();
-        if (tn < T) load(B, tn);
-        const int u = t / p.I;
-        const uint32_t mask = uniform(sm.umask[u]);
-        float acc[2][RMAX];
-#pragma unroll
-        for (int r = 0; r < RMAX; ++r) acc[0][r] = acc[1][r] = 0.0f;
-        wregs_dot<RFMT, ACT, RMAX, 2, CH>(A, p.H, 0, arow, mask, acc);
-        gu_store<ACT, RMAX>(p, sm, acc, t % p.I, mask, u, false, htag, hskip);
-        t = tn;
-        A = B;
-      }
-      return;
-    }
-  }
   for (int t = next(); t < T; t = next()) {
-    const int u = t / p.I, i = t % p.I;
-    gateup_task<ACT, RFMT, RMAX>(p, sm, p.routed, sm.U[u], i, p.I, uniform(sm.umask[u]), u, false, htag,
-                                 hskip);
+    const int u = t / nb, i0 = (t % nb) * GB;
+    const uint32_t mask = uniform(sm.umask[u]);
+    const int n = __popc(mask);
+    if (RMAX > 1 && n == 1)
+      gu_wide<ACT, RFMT, 1, GB>(p, sm, u, i0, mask, htag, hskip);
+    else if (RMAX > 1 && n == 2)
+      gu_wide<ACT, RFMT, 2, GB>(p, sm, u, i0, mask, htag, hskip);
+    else
+#pragma unroll 1
+      for (int g = 0; g < GB; ++g)
+        gateup_task<ACT, RFMT, RMAX>(p, sm, p.routed, sm.U[u], i0 + g, p.I, mask, u, false, htag,
+                                     hskip);
   }
 }
 
@@ -1873,42 +1898,34 @@ __device__ __forceinline__ bool ph_down(const Params& p, Smem& sm, uint32_t htag
  * Down phase of the fused launch at several rows. The shared expert is used by every row, so
  * its down rows cost R dot products per weight: each workgroup takes the shared rows of its own
  * hidden-position slice, as the per-slice down phase does. The routed down rows of all
- * distinct experts form one list of (expert, kRG consecutive output rows) quads, and workgroup
+ * distinct experts form one list of (expert, DG consecutive output rows) blocks, and workgroup
  * w takes an equal contiguous stretch of it, so a workgroup stages in LDS only the hidden rows
  * of the one or two experts its stretch touches (polling their tags) instead of all of them.
  * Every output y[h][r][slot] is published tagged; each workgroup then gathers the y values of
  * its slice and forms routed, shared and block as the per-slice down phase does. Each y value
- * comes from the same per-quad dot product as there, so the results are the same bits. */
+ * comes from the same per-row dot product as there, so the results are the same bits. */
 
-/* One quad: down rows hb .. hb + nr - 1 (nr <= kRG; the rest repeat the last row and are not
- * stored) of item `item` against its staged hidden rows; publishes y[h][r][slot]
- * (value bits | tag << 32) for every row r that uses the item. */
-template <int ACT, int FMT, int RMAX>
-__device__ __forceinline__ void em_down_task(const Params& p, const Smem& sm, const Mat& m, int e,
-                                             int inter, int item, int hb, int nr, bool is_shared,
-                                             int Kp, uint32_t tag) {
-  const int lane = threadIdx.x & 63;
-  constexpr int CH = Fmt<FMT>::CH_DN;
+/* Down rows hb .. hb + nr - 1 of expert e (nr <= kRG; the rest repeat the last row). */
+template <int FMT>
+__device__ __forceinline__ void em_rows(const Params& p, const Mat& m, int e, int inter, int hb,
+                                        int nr, const uint8_t* (&vr)[kRG],
+                                        const uint8_t* (&sr)[kRG]) {
   const size_t vb = row_vbytes(FMT, inter), sb = row_sbytes(FMT, inter);
-  const uint8_t* vr[kRG];
-  const uint8_t* sr[kRG];
 #pragma unroll
   for (int c = 0; c < kRG; ++c) {
     const size_t row = (size_t)e * p.H + hb + (c < nr ? c : nr - 1);
     vr[c] = m.down + row * vb;
     sr[c] = m.down_s ? m.down_s + row * sb : nullptr;
   }
-  const uint32_t mask = uniform(sm.umask[item]);
-  const void* arow[RMAX];
-#pragma unroll
-  for (int r = 0; r < RMAX; ++r)
-    arow[r] = sm.big + (size_t)((mask & (1u << r)) ? sm.voff[item][r] : 0) * 16;
-  float acc[kRG][RMAX];
-#pragma unroll
-  for (int c = 0; c < kRG; ++c)
-#pragma unroll
-    for (int r = 0; r < RMAX; ++r) acc[c][r] = 0.0f;
-  dot_rows<FMT, ACT, RMAX, kRG, CH>(vr, sr, inter, arow, mask, acc);
+}
+
+/* Publishes y[hb + c][r][slot] (value bits | tag << 32), c < nr, for every row r that uses
+ * item `item`, from the per-lane partial sums of the quad's rows. */
+template <int RMAX>
+__device__ __forceinline__ void em_store(const Params& p, const Smem& sm, float (&acc)[kRG][RMAX],
+                                         uint32_t mask, int item, int hb, int nr, bool is_shared,
+                                         int Kp, uint32_t tag) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int r = 0; r < RMAX; ++r) {
     if (!(mask & (1u << r))) continue;
@@ -1919,6 +1936,104 @@ __device__ __forceinline__ void em_down_task(const Params& p, const Smem& sm, co
       if (lane == c && c < nr)
         st_coh(p.y_part + ((size_t)(hb + c) * p.R + r) * Kp + slot,
                ((uint64_t)tag << 32) | __float_as_uint(t));
+    }
+  }
+}
+
+template <int RMAX>
+__device__ __forceinline__ void em_arows(const Smem& sm, int item, uint32_t mask,
+                                         const void* (&arow)[RMAX]) {
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r)
+    arow[r] = sm.big + (size_t)((mask & (1u << r)) ? sm.voff[item][r] : 0) * 16;
+}
+
+/* One quad: down rows hb .. hb + nr - 1 of item `item` against its staged hidden rows. */
+template <int ACT, int FMT, int RMAX>
+__device__ __forceinline__ void em_down_task(const Params& p, const Smem& sm, const Mat& m, int e,
+                                             int inter, int item, int hb, int nr, bool is_shared,
+                                             int Kp, uint32_t tag) {
+  constexpr int CH = Fmt<FMT>::CH_DN;
+  const uint8_t* vr[kRG];
+  const uint8_t* sr[kRG];
+  em_rows<FMT>(p, m, e, inter, hb, nr, vr, sr);
+  const uint32_t mask = uniform(sm.umask[item]);
+  const void* arow[RMAX];
+  em_arows<RMAX>(sm, item, mask, arow);
+  float acc[kRG][RMAX];
+#pragma unroll
+  for (int c = 0; c < kRG; ++c)
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) acc[c][r] = 0.0f;
+  dot_rows<FMT, ACT, RMAX, kRG, CH>(vr, sr, inter, arow, mask, acc);
+  em_store<RMAX>(p, sm, acc, mask, item, hb, nr, is_shared, Kp, tag);
+}
+
+/* DG down rows from hb of routed item `it` for the NA rows in `mask` (NA = its population),
+ * streamed at once against their staged hidden rows; publishes y[hb + c][r][slot]. */
+template <int ACT, int FMT, int NA, int DG>
+__device__ __forceinline__ void dn_wide(const Params& p, const Smem& sm, int it, int hb,
+                                        uint32_t mask, int Kp, uint32_t tag) {
+  const int lane = threadIdx.x & 63;
+  int rows[NA];
+  uint32_t m = mask;
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    rows[a] = __builtin_ctz(m);
+    m &= m - 1u;
+  }
+  const int e = sm.U[it];
+  const size_t vb = row_vbytes(FMT, p.I), sb = row_sbytes(FMT, p.I);
+  const uint8_t* vr[DG];
+  const uint8_t* sr[DG];
+#pragma unroll
+  for (int c = 0; c < DG; ++c) {
+    const size_t row = (size_t)e * p.H + hb + c;
+    vr[c] = p.routed.down + row * vb;
+    sr[c] = p.routed.down_s ? p.routed.down_s + row * sb : nullptr;
+  }
+  const void* arow[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) arow[a] = sm.big + (size_t)sm.voff[it][rows[a]] * 16;
+  float acc[DG][NA];
+#pragma unroll
+  for (int c = 0; c < DG; ++c)
+#pragma unroll
+    for (int a = 0; a < NA; ++a) acc[c][a] = 0.0f;
+  dot_rows<FMT, ACT, NA, DG, Fmt<FMT>::CH_DN>(vr, sr, p.I, arow, (1u << NA) - 1u, acc);
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    const int r = rows[a], slot = sm.uslot[it][r];
+#pragma unroll
+    for (int c = 0; c < DG; ++c) {
+      const float t = wave_sum(acc[c][a]);
+      if (lane == c)
+        st_coh(p.y_part + ((size_t)(hb + c) * p.R + r) * Kp + slot,
+               ((uint64_t)tag << 32) | __float_as_uint(t));
+    }
+  }
+}
+
+/* The routed blocks [qa, qb) of the staged group (block q: DG down rows from (q % nqi) DG of
+ * the expert q / nqi), claimed one at a time by the waves. When one or two rows use the expert,
+ * the DG rows stream at once against their hidden rows; otherwise they go kRG at a time for
+ * every row that uses it. sm.down_next must be zero and visible to every wave. */
+template <int ACT, int FMT, int RMAX>
+__device__ __forceinline__ void em_routed_blocks(const Params& p, Smem& sm, int qa, int qb,
+                                                 int nqi, int Kp, uint32_t tag) {
+  constexpr int DG = Wide<FMT>::DG;
+  for (int q = qa + claim(&sm.down_next); q < qb; q = qa + claim(&sm.down_next)) {
+    const int it = q / nqi, hb = (q % nqi) * DG;
+    const uint32_t mask = uniform(sm.umask[it]);
+    const int n = __popc(mask);
+    if (n == 1) {
+      dn_wide<ACT, FMT, 1, DG>(p, sm, it, hb, mask, Kp, tag);
+    } else if (n == 2) {
+      dn_wide<ACT, FMT, 2, DG>(p, sm, it, hb, mask, Kp, tag);
+    } else {
+#pragma unroll 1
+      for (int h = hb; h < hb + DG; h += kRG)
+        em_down_task<ACT, FMT, RMAX>(p, sm, p.routed, sm.U[it], p.I, it, h, kRG, false, Kp, tag);
     }
   }
 }
@@ -1970,7 +2085,7 @@ __device__ __forceinline__ bool ph_down_em(const Params& p, Smem& sm, uint32_t h
   const uint32_t tag = (uint32_t)(sm.epoch + 1);
   const int nU = sm.nU, Kp = p.K + (p.Is > 0 ? 1 : 0), off = p.Is > 0 ? 1 : 0;
   const size_t ab = ACT == F32 ? 4 : 2;
-  const int nqi = p.H / kRG;
+  const int nqi = p.H / Wide<RFMT>::DG; /* routed down blocks per expert */
   const Slice c = slice_of(p);
   SliceRegs sreg;
   slice_prefetch<ACT>(p, c, sreg);
@@ -1988,8 +2103,9 @@ __device__ __forceinline__ bool ph_down_em(const Params& p, Smem& sm, uint32_t h
       em_down_task<ACT, SFMT, RMAX>(p, sm, p.shared, 0, p.Is, nU, c.h0 + t * kRG, nr, true, Kp,
                                     tag);
     }
+    stamp(p, sm.trace_on != 0, 20);
   }
-  /* this workgroup's stretch of routed quads */
+  /* this workgroup's stretch of routed blocks */
   const long QR = (long)nU * nqi;
   const int q0 = (int)(QR * blockIdx.x / gridDim.x), q1 = (int)(QR * (blockIdx.x + 1) / gridDim.x);
   int u = q0 / nqi;
@@ -1997,6 +2113,7 @@ __device__ __forceinline__ bool ph_down_em(const Params& p, Smem& sm, uint32_t h
   while (u < uend) {
     const int u1 = down_group_end(p, sm, u + off, ab, uend - u) - off;
     if (!first) __syncthreads(); /* the previous items' tasks are done with the staging area */
+    if (tid == 0) sm.down_next = 0; /* visible after stage_list's barrier */
     stage_list(p, sm, u + off, u1 + off, ab);
     if (!stage_copy<ACT>(p, sm, true, htag)) return false;
     if (first) {
@@ -2005,14 +2122,11 @@ __device__ __forceinline__ bool ph_down_em(const Params& p, Smem& sm, uint32_t h
       first = false;
     }
     const int qa = q0 > u * nqi ? q0 : u * nqi, qb = q1 < u1 * nqi ? q1 : u1 * nqi;
-    for (int q = qa + wave; q < qb; q += kWaves) {
-      const int it = q / nqi;
-      em_down_task<ACT, RFMT, RMAX>(p, sm, p.routed, sm.U[it], p.I, it, (q % nqi) * kRG, kRG,
-                                    false, Kp, tag);
-    }
+    em_routed_blocks<ACT, RFMT, RMAX>(p, sm, qa, qb, nqi, Kp, tag);
     u = u1;
   }
   if (first) slice_store(p, c, sm, sreg);
+  stamp(p, sm.trace_on != 0, 10);
   const DownGeo g = down_geo(p, sm);
   if (!em_gather_y(p, sm, g.h0, g.nh, Kp, g.y, tag)) return false;
   for (int q = tid; q < g.nh * R; q += kBlock) {
@@ -2305,8 +2419,9 @@ __global__ void __launch_bounds__(kBlock) k_expand(Params p) {
  *   partials (tagged; workgroup q sums carry output q over the grid).
  * Trace slots: 0 start, 1 mix partials, 2 pre-side inputs ready, 3 pre side, 4 router,
  * 5 shared gate/up, 6 select rows, 7 select finished, 8 plan, 9 routed gate/up,
- * 11 down + block, 12 expand, 13 carry; 14-18 inside the pre side, 19 select scores,
- * 21 first down group staged, 22-24 router start, router dots, logits gathered. */
+ * 10 routed down (several rows), 11 down + block, 12 expand, 13 carry; 14-18 inside the pre
+ * side, 19 select scores, 20 shared down (several rows), 21 first down group staged, 22-24
+ * router start, router dots, logits gathered, 25-31 gate/up end of waves 1-7. */
 template <int ACT, int RFMT, int SFMT, int RMAX>
 __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   __shared__ Smem sm;
