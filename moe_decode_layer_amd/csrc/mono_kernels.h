@@ -172,7 +172,7 @@ __device__ __forceinline__ bool coh_copy_tagged_to_lds(const uint64_t* src, int 
   if (tid == 0) *flag = 1;
   __syncthreads();
   bool ok = true;
-  constexpr int B = 4;
+  constexpr int B = 8;
   for (int v0 = 0; v0 < npair; v0 += B * kBlock) {
     uint4 buf[B];
 #pragma unroll
@@ -1603,18 +1603,21 @@ __device__ __forceinline__ int down_item(const Params& p, const Smem& sm, int k)
   return p.Is > 0 ? (k == 0 ? sm.nU : k - 1) : k;
 }
 
-/* End of the group of items [k0, end): as many as fit the staging area, at most max_items. */
+/* End of the group of items [k0, end): as many as fit the staging area next to used0 bytes and
+ * count0 rows already listed, at most max_items. */
 __device__ __forceinline__ int down_group_end(const Params& p, const Smem& sm, int k0, size_t ab,
-                                              int max_items) {
+                                              int max_items, size_t used0 = 0, int count0 = 0) {
   const int nU = sm.nU, n_items = nU + (p.Is > 0 ? 1 : 0);
-  int k = k0, count = 0;
-  size_t used = 0;
+  int k = k0, count = count0;
+  size_t used = used0;
   while (k < n_items && k - k0 < max_items) {
     const int item = down_item(p, sm, k);
     const int inter = item == nU ? p.Is : p.I;
     const int rows = __popc(sm.umask[item]);
     const size_t need = (size_t)rows * inter * ab;
-    if (k > k0 && (used + need > (size_t)kLdsHidBytes || count + rows > kMaxStaged)) break;
+    /* the first item always fits an empty area; rows already staged (used0) may leave none */
+    if ((k > k0 || count0 > 0) && (used + need > (size_t)kLdsHidBytes || count + rows > kMaxStaged))
+      break;
     used += need;
     count += rows;
     ++k;
@@ -1680,19 +1683,24 @@ __device__ __forceinline__ void slice_store(const Params& p, const Slice& c, Sme
   }
 }
 
-/* Staging list of the items of positions [first, last) in down_item order: for every (item, row
+/* Staging list of the items of positions [first, last) in down_item order (optionally led by
+ * the shared expert): for every (item, row
  * that uses it), in item-major
  * order, the source of the hidden row (routed [R][K][I] or shared [R][Is]), its LDS offset and
  * length in 16-byte units, and sm.voff. One wave scans the items 64 at a time. */
 __device__ __forceinline__ void stage_list(const Params& p, Smem& sm, int first, int last,
-                                           size_t ab) {
+                                           size_t ab, bool lead_shared = false) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x, nU = sm.nU;
+    /* with lead_shared the shared expert (position 0) comes before positions [first, last) */
+    const int lead = lead_shared ? 1 : 0, n = lead + (last - first);
     int nv = 0;
     uint32_t off = 0;
-    for (int k0 = first; k0 < last; k0 += 64) {
-      const bool live = k0 + lane < last;
-      const int it = live ? down_item(p, sm, k0 + lane) : 0;
+    for (int k0 = 0; k0 < n; k0 += 64) {
+      const int v0 = k0 + lane;
+      const bool live = v0 < n;
+      const int pos = v0 < lead ? 0 : first + v0 - lead;
+      const int it = live ? down_item(p, sm, pos) : 0;
       const uint32_t m = live ? sm.umask[it] : 0u;
       const bool sh = it == nU;
       const uint32_t vl = (uint32_t)((size_t)(sh ? p.Is : p.I) * ab / 16);
@@ -2079,6 +2087,35 @@ __device__ __forceinline__ bool em_gather_y(const Params& p, Smem& sm, int h0, i
   return all;
 }
 
+/* Relative cost of a routed down block by the number of rows that use its expert: the wide
+ * path streams the rows once for one or two rows; more rows take the general path. */
+__device__ __forceinline__ uint32_t em_cost(int n) { return n == 1 ? 2u : n == 2 ? 3u : 2u + n; }
+
+/* Workgroup b's stretch [q0, q1) of the nU * nqi routed blocks: the list is cut at the blocks
+ * whose cost prefix first reaches b / grid and (b + 1) / grid of the total, so every workgroup
+ * gets the same cost and the stretches tile the list. */
+__device__ __forceinline__ void em_stretch(const Smem& sm, int nqi, int& q0, int& q1) {
+  const int nU = sm.nU, G = gridDim.x, b = blockIdx.x;
+  uint64_t W = 0;
+  for (int u = 0; u < nU; ++u) W += (uint64_t)nqi * em_cost(__popc(sm.umask[u]));
+  const uint64_t c0 = W * b / G, c1 = W * (b + 1) / G;
+  q0 = q1 = nU * nqi;
+  bool f0 = false, f1 = false;
+  uint64_t P = 0;
+  for (int u = 0; u < nU && !f1; ++u) {
+    const uint64_t w = em_cost(__popc(sm.umask[u])), Pn = P + (uint64_t)nqi * w;
+    if (!f0 && c0 < Pn) {
+      q0 = u * nqi + (int)((c0 - P + w - 1) / w);
+      f0 = true;
+    }
+    if (c1 < Pn) {
+      q1 = u * nqi + (int)((c1 - P + w - 1) / w);
+      f1 = true;
+    }
+    P = Pn;
+  }
+}
+
 template <int ACT, int RFMT, int SFMT, int RMAX>
 __device__ __forceinline__ bool ph_down_em(const Params& p, Smem& sm, uint32_t htag) {
   const int tid = threadIdx.x, wave = tid >> 6, R = p.R;
@@ -2089,40 +2126,41 @@ __device__ __forceinline__ bool ph_down_em(const Params& p, Smem& sm, uint32_t h
   const Slice c = slice_of(p);
   SliceRegs sreg;
   slice_prefetch<ACT>(p, c, sreg);
-  bool first = true;
-  /* the shared expert's down rows of this workgroup's slice (its hidden rows are complete
-   * since before the select) */
-  if (p.Is > 0 && c.nh > 0) {
-    stage_list(p, sm, 0, 1, ab);
-    if (!stage_copy<ACT>(p, sm, true, htag)) return false;
-    slice_store(p, c, sm, sreg);
-    stamp(p, sm.trace_on != 0, 21);
-    first = false;
-    for (int t = wave; t * kRG < c.nh; t += kWaves) {
-      const int nr = c.nh - t * kRG < kRG ? c.nh - t * kRG : kRG;
-      em_down_task<ACT, SFMT, RMAX>(p, sm, p.shared, 0, p.Is, nU, c.h0 + t * kRG, nr, true, Kp,
-                                    tag);
-    }
-    stamp(p, sm.trace_on != 0, 20);
-  }
   /* this workgroup's stretch of routed blocks */
-  const long QR = (long)nU * nqi;
-  const int q0 = (int)(QR * blockIdx.x / gridDim.x), q1 = (int)(QR * (blockIdx.x + 1) / gridDim.x);
+  int q0, q1;
+  em_stretch(sm, nqi, q0, q1);
   int u = q0 / nqi;
   const int uend = q1 > q0 ? (q1 - 1) / nqi + 1 : u;
-  while (u < uend) {
-    const int u1 = down_group_end(p, sm, u + off, ab, uend - u) - off;
+  /* the first staged group holds the shared expert's hidden rows (for this workgroup's slice of
+   * its down rows, complete since before the select) and as many routed items as fit beside
+   * them; the waves take the shared rows first, then claim routed blocks */
+  const bool has_sh = p.Is > 0 && c.nh > 0;
+  bool first = true;
+  while (u < uend || (first && has_sh)) {
+    const bool with_sh = first && has_sh;
+    const size_t sh_bytes = with_sh ? (size_t)R * p.Is * ab : 0;
+    const int u1 = u < uend ? down_group_end(p, sm, u + off, ab, uend - u, sh_bytes,
+                                             with_sh ? R : 0) - off
+                            : u;
     if (!first) __syncthreads(); /* the previous items' tasks are done with the staging area */
     if (tid == 0) sm.down_next = 0; /* visible after stage_list's barrier */
-    stage_list(p, sm, u + off, u1 + off, ab);
+    stage_list(p, sm, u + off, u1 + off, ab, with_sh);
     if (!stage_copy<ACT>(p, sm, true, htag)) return false;
     if (first) {
       slice_store(p, c, sm, sreg);
       stamp(p, sm.trace_on != 0, 21);
       first = false;
     }
+    if (with_sh) {
+      for (int t = wave; t * kRG < c.nh; t += kWaves) {
+        const int nr = c.nh - t * kRG < kRG ? c.nh - t * kRG : kRG;
+        em_down_task<ACT, SFMT, RMAX>(p, sm, p.shared, 0, p.Is, nU, c.h0 + t * kRG, nr, true,
+                                      Kp, tag);
+      }
+      stamp(p, sm.trace_on != 0, 20);
+    }
     const int qa = q0 > u * nqi ? q0 : u * nqi, qb = q1 < u1 * nqi ? q1 : u1 * nqi;
-    em_routed_blocks<ACT, RFMT, RMAX>(p, sm, qa, qb, nqi, Kp, tag);
+    if (qa < qb) em_routed_blocks<ACT, RFMT, RMAX>(p, sm, qa, qb, nqi, Kp, tag);
     u = u1;
   }
   if (first) slice_store(p, c, sm, sreg);
@@ -2457,13 +2495,22 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   ph_router<ACT, RMAX, true>(p, sm, rpre, tag, sm.skip_phase == PH_ROUTER);
   stamp(p, tr, 4);
   ph_sinkhorn(p, sm, blockIdx.x == 0); /* comb is needed only by the expand */
-  select_rows(p, sm, blockIdx.x == 0, true, tag);
-  stamp(p, tr, 6);
   /* hidden rows carry a 16-bit tag of this launch (never 0, the value the init leaves) */
   const uint32_t htag = (uint32_t)(sm.epoch % 65535u) + 1u;
   const bool hskip = sm.skip_phase == PH_GATEUP; /* fault injection: store no hidden rows */
-  ph_gateup_shared_claim<ACT, SFMT, RMAX>(p, sm, htag, hskip);
-  stamp(p, tr, 5);
+  if (RMAX == 1) {
+    /* one row: wave 0 selects while the other waves take the shared expert's rows */
+    select_rows(p, sm, blockIdx.x == 0, true, tag);
+    stamp(p, tr, 6);
+    ph_gateup_shared_claim<ACT, SFMT, RMAX>(p, sm, htag, hskip);
+    stamp(p, tr, 5);
+  } else {
+    /* several rows: most waves select, so the shared rows go first, while the logits arrive */
+    ph_gateup_shared_claim<ACT, SFMT, RMAX>(p, sm, htag, hskip);
+    stamp(p, tr, 5);
+    select_rows(p, sm, blockIdx.x == 0, true, tag);
+    stamp(p, tr, 6);
+  }
   __syncthreads();
   if (!select_finish(p, sm, blockIdx.x == 0)) return;
   stamp(p, tr, 7);
