@@ -97,7 +97,8 @@ struct Params {
   uint64_t* mix_part; /* [nchunk][R][25] tagged mix partial sums: value bits | tag << 32 */
   float* carry_part; /* [R * 25][grid] tagged partials: value bits | epoch tag << 32 */
   uint64_t* pre_done; /* [grid] launch tag of each workgroup once it has read all of the state */
-  uint64_t* y_part;   /* [R][K + 1][H] tagged down-projection outputs (slot K: shared expert) */
+  uint64_t* y_part;   /* [R][Kp][H] tagged down-projection outputs, Kp = K + (shared expert ? 1
+                       * : 0), slot K the shared expert */
   uint64_t* lgp;     /* [parts][R][E] tagged router logit parts (same format) */
   uint64_t* trace;   /* [grid][32] real-time stamps */
   size_t tag_words; /* u64 words from carry_part through lgp cleared by the workspace init */

@@ -1475,17 +1475,21 @@ __device__ __forceinline__ void gu_wide(const Params& p, const Smem& sm, int u, 
 #pragma unroll
     for (int a = 0; a < NA; ++a) acc[k][a] = 0.0f;
   dot_rows<FMT, ACT, NA, 2 * GB, Fmt<FMT>::CH_GU>(vr, sr, p.H, arow, (1u << NA) - 1u, acc);
+  /* lane g stores hidden row i0 + g: one coalesced store per row */
 #pragma unroll
-  for (int g = 0; g < GB; ++g)
+  for (int a = 0; a < NA; ++a) {
+    const int r = rows[a];
+    float hv = 0.0f;
 #pragma unroll
-    for (int a = 0; a < NA; ++a) {
-      const int r = rows[a];
+    for (int g = 0; g < GB; ++g) {
       const float gg = act_round<ACT>(wave_sum(acc[2 * g][a]));
       const float uu = act_round<ACT>(wave_sum(acc[2 * g + 1][a]));
       const float h = act_round<ACT>(gg / (1.0f + expf(-gg)) * uu);
-      if (lane == 0 && !hskip)
-        hid_store<ACT>(p.h_routed, ((size_t)r * p.K + sm.uslot[u][r]) * p.I + i0 + g, h, htag);
+      if (lane == g) hv = h;
     }
+    if (lane < GB && !hskip)
+      hid_store<ACT>(p.h_routed, ((size_t)r * p.K + sm.uslot[u][r]) * p.I + i0 + lane, hv, htag);
+  }
 }
 
 /* Routed gate/up: workgroup b owns tasks b, b + grid, ... (expert-major order), so at any
@@ -1909,7 +1913,7 @@ __device__ __forceinline__ bool ph_down(const Params& p, Smem& sm, uint32_t htag
  * distinct experts form one list of (expert, DG consecutive output rows) blocks, and workgroup
  * w takes an equal contiguous stretch of it, so a workgroup stages in LDS only the hidden rows
  * of the one or two experts its stretch touches (polling their tags) instead of all of them.
- * Every output y[h][r][slot] is published tagged; each workgroup then gathers the y values of
+ * Every output y[r][slot][h] is published tagged; each workgroup then gathers the y values of
  * its slice and forms routed, shared and block as the per-slice down phase does. Each y value
  * comes from the same per-row dot product as there, so the results are the same bits. */
 
@@ -1927,7 +1931,7 @@ __device__ __forceinline__ void em_rows(const Params& p, const Mat& m, int e, in
   }
 }
 
-/* Publishes y[hb + c][r][slot] (value bits | tag << 32), c < nr, for every row r that uses
+/* Publishes y[r][slot][hb + c] (value bits | tag << 32), c < nr, for every row r that uses
  * item `item`, from the per-lane partial sums of the quad's rows. */
 template <int RMAX>
 __device__ __forceinline__ void em_store(const Params& p, const Smem& sm, float (&acc)[kRG][RMAX],
@@ -1942,7 +1946,7 @@ __device__ __forceinline__ void em_store(const Params& p, const Smem& sm, float 
     for (int c = 0; c < kRG; ++c) {
       const float t = wave_sum(acc[c][r]);
       if (lane == c && c < nr)
-        st_coh(p.y_part + ((size_t)(hb + c) * p.R + r) * Kp + slot,
+        st_coh(p.y_part + ((size_t)r * Kp + slot) * p.H + hb + c,
                ((uint64_t)tag << 32) | __float_as_uint(t));
     }
   }
@@ -1978,7 +1982,7 @@ __device__ __forceinline__ void em_down_task(const Params& p, const Smem& sm, co
 }
 
 /* DG down rows from hb of routed item `it` for the NA rows in `mask` (NA = its population),
- * streamed at once against their staged hidden rows; publishes y[hb + c][r][slot]. */
+ * streamed at once against their staged hidden rows; publishes y[r][slot][hb + c]. */
 template <int ACT, int FMT, int NA, int DG>
 __device__ __forceinline__ void dn_wide(const Params& p, const Smem& sm, int it, int hb,
                                         uint32_t mask, int Kp, uint32_t tag) {
@@ -2016,7 +2020,7 @@ __device__ __forceinline__ void dn_wide(const Params& p, const Smem& sm, int it,
     for (int c = 0; c < DG; ++c) {
       const float t = wave_sum(acc[c][a]);
       if (lane == c)
-        st_coh(p.y_part + ((size_t)(hb + c) * p.R + r) * Kp + slot,
+        st_coh(p.y_part + ((size_t)r * Kp + slot) * p.H + hb + c,
                ((uint64_t)tag << 32) | __float_as_uint(t));
     }
   }
@@ -2046,22 +2050,24 @@ __device__ __forceinline__ void em_routed_blocks(const Params& p, Smem& sm, int 
   }
 }
 
-/* Gathers the tagged y values of the slice, [nh][R][Kp], into LDS at dst as floats, polling
- * (bounded) until each carries `tag`. Whole workgroup; returns false (uniform) on expiry. */
+/* Gathers the tagged y values of the slice (y_part is [R][Kp][H]) into LDS at dst as floats,
+ * [nh][R][Kp], polling (bounded) until each carries `tag`. Whole workgroup; returns false
+ * (uniform) on expiry. */
 __device__ __forceinline__ bool em_gather_y(const Params& p, Smem& sm, int h0, int nh, int Kp,
                                             float* dst, uint32_t tag) {
   const int tid = threadIdx.x;
   const int n = nh * p.R * Kp;
-  const __amdgpu_buffer_rsrc_t yr =
-      coh_region(p.y_part + (size_t)h0 * p.R * Kp, (size_t)(n > 0 ? n : 1) * 8);
+  const __amdgpu_buffer_rsrc_t yr = coh_region(p.y_part, (size_t)p.R * Kp * p.H * 8);
   int ok = 1;
   constexpr int B = 4;
   for (int v0 = 0; v0 < n; v0 += B * kBlock) {
     uint2 b[B];
+    uint32_t off[B];
 #pragma unroll
     for (int k = 0; k < B; ++k) {
-      const int v = v0 + k * kBlock + tid;
-      if (v < n) b[k] = coh_b64(yr, (uint32_t)v * 8u);
+      const int v = v0 + k * kBlock + tid; /* v = (r Kp + slot) nh + hl */
+      off[k] = (uint32_t)(((size_t)(v / nh) * p.H + h0 + v % nh) * 8);
+      if (v < n) b[k] = coh_b64(yr, off[k]);
     }
 #pragma unroll
     for (int k = 0; k < B; ++k) {
@@ -2072,14 +2078,15 @@ __device__ __forceinline__ bool em_gather_y(const Params& p, Smem& sm, int h0, i
         while (b[k].y != tag) {
           asm volatile("" ::: "memory");
           __builtin_amdgcn_s_sleep(1);
-          b[k] = coh_b64(yr, (uint32_t)v * 8u);
+          b[k] = coh_b64(yr, off[k]);
           if (__builtin_amdgcn_s_memrealtime() - t0 > sm.spin) {
             ok = 0;
             break;
           }
         }
       }
-      dst[v] = __uint_as_float(b[k].x);
+      const int rs = v / nh, hl = v % nh; /* rs = r Kp + slot */
+      dst[((size_t)hl * p.R + rs / Kp) * Kp + rs % Kp] = __uint_as_float(b[k].x);
     }
   }
   const bool all = __syncthreads_and(ok) != 0;
