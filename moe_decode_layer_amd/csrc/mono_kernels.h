@@ -1441,12 +1441,16 @@ __device__ __forceinline__ void ph_gateup_shared_claim(const Params& p, Smem& sm
   }
 }
 
+template <int ACT, int NA, int GB>
+__device__ __forceinline__ void gu_wide_store(const Params& p, const Smem& sm,
+                                              float (&acc)[2 * GB][NA], int u, int i0,
+                                              const int (&rows)[NA], uint32_t htag, bool hskip);
+
 /* GB consecutive hidden rows i0 .. of routed expert u for the NA rows in `mask` (NA = its
  * population): the 2 GB gate and up weight rows stream at once. */
 template <int ACT, int FMT, int NA, int GB>
 __device__ __forceinline__ void gu_wide(const Params& p, const Smem& sm, int u, int i0,
                                         uint32_t mask, uint32_t htag, bool hskip) {
-  const int lane = threadIdx.x & 63;
   int rows[NA];
   uint32_t m = mask;
 #pragma unroll
@@ -1475,7 +1479,17 @@ __device__ __forceinline__ void gu_wide(const Params& p, const Smem& sm, int u, 
 #pragma unroll
     for (int a = 0; a < NA; ++a) acc[k][a] = 0.0f;
   dot_rows<FMT, ACT, NA, 2 * GB, Fmt<FMT>::CH_GU>(vr, sr, p.H, arow, (1u << NA) - 1u, acc);
-  /* lane g stores hidden row i0 + g: one coalesced store per row */
+  gu_wide_store<ACT, NA, GB>(p, sm, acc, u, i0, rows, htag, hskip);
+}
+
+/* SwiGLU of hidden rows i0 .. i0 + GB - 1 of item u for rows[0 .. NA) from the per-lane partial
+ * sums of their gate (acc[2 g]) and up (acc[2 g + 1]) rows; lane g stores hidden row i0 + g,
+ * one coalesced store per row. */
+template <int ACT, int NA, int GB>
+__device__ __forceinline__ void gu_wide_store(const Params& p, const Smem& sm,
+                                              float (&acc)[2 * GB][NA], int u, int i0,
+                                              const int (&rows)[NA], uint32_t htag, bool hskip) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int a = 0; a < NA; ++a) {
     const int r = rows[a];
@@ -1498,9 +1512,105 @@ __device__ __forceinline__ void gu_wide(const Params& p, const Smem& sm, int u, 
  * task is GB consecutive hidden rows of one expert: when one or two rows use the expert, all
  * 2 GB weight rows stream at once against them; otherwise the rows go one by one for every row
  * that uses the expert. Every hidden value comes from the same per-row dot product either way. */
+/* Routed gate/up at several rows for Q8_0 and MXFP4 rows that fit one chunk: tasks of GB / 2
+ * hidden rows, software-pipelined over two register buffers, so a wave issues the loads of its
+ * next task before it computes the current one and waits only for the current one's loads
+ * (every load is issued unconditionally: past the last task a wave loads through an empty
+ * resource, which returns zeros without touching memory). */
+template <int ACT, int FMT, int RMAX>
+__device__ __forceinline__ void gu_pipelined(const Params& p, Smem& sm, uint32_t htag,
+                                             bool hskip) {
+  constexpr int GBp = Wide<FMT>::GB / 2, NR = 2 * GBp, CH = Fmt<FMT>::CH_GU;
+  const int lane = threadIdx.x & 63;
+  const int nb = p.I / GBp, T = sm.nU * nb;
+  const size_t vb = row_vbytes(FMT, p.H), sb = row_sbytes(FMT, p.H);
+  auto next = [&]() -> int { return (int)blockIdx.x + claim(&sm.routed_next) * (int)gridDim.x; };
+  auto load = [&](WRegs<FMT, NR, CH>& W, int t) {
+    const bool live = t < T;
+    const int tt = live ? t : 0;
+    const int u = tt / nb, i0 = (tt % nb) * GBp;
+#pragma unroll
+    for (int g = 0; g < GBp; ++g) {
+      const uint8_t* vr[2];
+      const uint8_t* sr[2];
+      gu_rows<FMT>(p, p.routed, sm.U[u], i0 + g, p.I, vr, sr);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const __amdgpu_buffer_rsrc_t rv = row_rsrc(vr[h], live ? vb : 0);
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(sr[h], live ? sb : 0);
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+          wload<FMT>(rv, rs, c, lane, W.v[2 * g + h][c], W.sc[2 * g + h][c]);
+      }
+    }
+  };
+  auto compute = [&](const WRegs<FMT, NR, CH>& W, int t) {
+    const int u = t / nb, i0 = (t % nb) * GBp;
+    const uint32_t mask = uniform(sm.umask[u]);
+    const int n = __popc(mask);
+    const size_t ab = ACT == F32 ? 4 : 2;
+    if (n == 1) {
+      const int rows[1] = {__builtin_ctz(mask)};
+      const void* arow[1] = {sm.big + (size_t)rows[0] * p.H * ab};
+      float acc[NR][1];
+#pragma unroll
+      for (int k = 0; k < NR; ++k) acc[k][0] = 0.0f;
+      wregs_dot<FMT, ACT, 1, NR, CH>(W, p.H, 0, arow, 1u, acc);
+      gu_wide_store<ACT, 1, GBp>(p, sm, acc, u, i0, rows, htag, hskip);
+    } else if (n == 2) {
+      const int r0 = __builtin_ctz(mask);
+      const int rows[2] = {r0, __builtin_ctz(mask & (mask - 1u))};
+      const void* arow[2] = {sm.big + (size_t)rows[0] * p.H * ab,
+                             sm.big + (size_t)rows[1] * p.H * ab};
+      float acc[NR][2];
+#pragma unroll
+      for (int k = 0; k < NR; ++k) acc[k][0] = acc[k][1] = 0.0f;
+      wregs_dot<FMT, ACT, 2, NR, CH>(W, p.H, 0, arow, 3u, acc);
+      gu_wide_store<ACT, 2, GBp>(p, sm, acc, u, i0, rows, htag, hskip);
+    } else {
+      const void* arow[RMAX];
+      act_rows_ptrs<ACT, RMAX>(p, sm, arow);
+      float acc[NR][RMAX];
+#pragma unroll
+      for (int k = 0; k < NR; ++k)
+#pragma unroll
+        for (int r = 0; r < RMAX; ++r) acc[k][r] = 0.0f;
+      wregs_dot<FMT, ACT, RMAX, NR, CH>(W, p.H, 0, arow, mask, acc);
+#pragma unroll
+      for (int g = 0; g < GBp; ++g) {
+        float a2[2][RMAX];
+#pragma unroll
+        for (int r = 0; r < RMAX; ++r) {
+          a2[0][r] = acc[2 * g][r];
+          a2[1][r] = acc[2 * g + 1][r];
+        }
+        gu_store<ACT, RMAX>(p, sm, a2, i0 + g, mask, u, false, htag, hskip);
+      }
+    }
+  };
+  WRegs<FMT, NR, CH> A, B;
+  int tA = next();
+  load(A, tA);
+  while (tA < T) {
+    const int tB = next();
+    load(B, tB);
+    compute(A, tA);
+    if (tB >= T) break;
+    tA = next();
+    load(A, tA);
+    compute(B, tB);
+  }
+}
+
 template <int ACT, int RFMT, int RMAX>
 __device__ __forceinline__ void ph_gateup_routed(const Params& p, Smem& sm, uint32_t htag,
                                                  bool hskip) {
+  if constexpr (RMAX > 1 && (RFMT == Q8 || RFMT == FP4)) {
+    if (p.H <= 64 * Fmt<RFMT>::EL * Fmt<RFMT>::CH_GU) {
+      gu_pipelined<ACT, RFMT, RMAX>(p, sm, htag, hskip);
+      return;
+    }
+  }
   constexpr int GB = RMAX > 1 ? Wide<RFMT>::GB : 1;
   const int nb = p.I / GB;
   const int T = sm.nU * nb;
