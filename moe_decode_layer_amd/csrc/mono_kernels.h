@@ -505,7 +505,10 @@ struct Smem {
   int sel_ok;      /* cleared when a select wave's logits did not arrive */
   int shared_next; /* next shared-expert gate/up task of this workgroup (fused launch) */
   int routed_next; /* next routed gate/up task of this workgroup (fused launch) */
-  int down_next;   /* next down block of the current staged group (fused launch, several rows) */
+  int down_next;   /* next down block of the current staged group (fused launch, several rows),
+                      or next down task of the one-row flow */
+  int stage_state[kMaxUnion + 1]; /* one-row flow: item staged? 0 no, 1 being staged, 2 yes,
+                                     3 its hidden rows did not arrive */
   int nU;
   int flag;
   uint64_t epoch;
@@ -1941,6 +1944,188 @@ __device__ __forceinline__ bool stage_copy(const Params& p, Smem& sm, bool check
   return true;
 }
 
+/* Per (h, r) of the slice, from y [hs][R][K + 1] in LDS: routed = f32 sum_j w_j y_j in
+ * selection order, shared = rounded y_s, block = rounded (routed + shared); block also to LDS
+ * for the expand. Whole workgroup. */
+template <int ACT>
+__device__ __forceinline__ void down_combine(const Params& p, Smem& sm, const DownGeo& g) {
+  const int R = p.R;
+  for (int q = threadIdx.x; q < g.nh * R; q += kBlock) {
+    const int hl = q / R, r = q % R;
+    const float* y = g.y + ((size_t)hl * R + r) * (p.K + 1);
+    float routed = 0.0f;
+    for (int j = 0; j < p.K; ++j) routed = fmaf(sm.sel_w[r][j], y[j], routed);
+    const float shared = p.Is > 0 ? act_round<ACT>(y[p.K]) : 0.0f;
+    const float blk = act_round<ACT>(routed + shared);
+    const size_t o = (size_t)r * p.H + g.h0 + hl;
+    if (p.routed_out) p.routed_out[o] = routed;
+    if (p.shared_out) act_st<ACT>(p.shared_out, o, shared);
+    if (p.block) act_st<ACT>(p.block, o, blk);
+    g.blk[q] = blk;
+  }
+  __syncthreads();
+}
+
+/* ------------------------------------------------------------------------------------------
+ * One-row down phase of the fused launch as a flow: a wave that runs out of gate/up tasks goes
+ * straight on to down tasks (item, kFlowRows rows of the slice) claimed from an LDS counter, while
+ * other waves still finish their gate/up rows. Each item's hidden row is staged in LDS, behind
+ * the activation row, by the first wave that needs it (an LDS compare-and-swap elects it);
+ * other waves needing the item wait on its LDS state. Used when every item fits at once. */
+
+/* LDS byte offset of the hidden rows of the item at down position k. */
+__device__ __forceinline__ uint32_t flow_off(const Params& p, int k, size_t ab) {
+  const size_t base = ((size_t)p.R * p.H * ab + 15) / 16 * 16;
+  if (p.Is > 0) return (uint32_t)(k == 0 ? base : base + (size_t)p.Is * ab + (size_t)(k - 1) * p.I * ab);
+  return (uint32_t)(base + (size_t)k * p.I * ab);
+}
+
+__device__ __forceinline__ bool flow_fits(const Params& p, const Smem& sm, size_t ab) {
+  const int n_items = sm.nU + (p.Is > 0 ? 1 : 0);
+  return p.R == 1 && flow_off(p, n_items, ab) <= (uint32_t)kLdsHidBytes;
+}
+
+/* One wave copies the hidden row of item `item` (one row) into LDS at byte offset `off`,
+ * dropping the tags, each 16-byte chunk polled (bounded) until its tags are `tag`. */
+template <int ACT>
+__device__ __forceinline__ bool flow_stage(const Params& p, Smem& sm, int item, uint32_t off,
+                                           uint32_t tag) {
+  const int lane = threadIdx.x & 63, nU = sm.nU;
+  constexpr int TB = ACT == F32 ? 8 : 4, EPC = ACT == F32 ? 4 : 8;
+  const bool sh = item == nU;
+  const int inter = sh ? p.Is : p.I;
+  const int r = __builtin_ctz(sm.umask[item]);
+  const size_t src0 = sh ? (size_t)r * p.Is : ((size_t)r * p.K + sm.uslot[item][r]) * p.I;
+  const __amdgpu_buffer_rsrc_t rs =
+      sh ? coh_region(p.h_shared, (size_t)p.R * p.Is * TB)
+         : coh_region(p.h_routed, (size_t)p.R * p.K * p.I * TB);
+  const int nch = inter / EPC; /* 16-byte LDS chunks */
+  bool ok = true;
+  constexpr int B = 8;
+  for (int c0 = 0; c0 < nch; c0 += B * 64) {
+    uint4 lo[B], hi[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int c = c0 + b * 64 + lane;
+      const uint32_t o = (uint32_t)((src0 + (size_t)c * EPC) * TB);
+      if (c < nch) {
+        lo[b] = coh_b128(rs, o);
+        hi[b] = coh_b128(rs, o + 16);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int c = c0 + b * 64 + lane;
+      if (c >= nch) continue;
+      auto stale = [&]() {
+        if (ACT == F32)
+          return lo[b].y != tag || lo[b].w != tag || hi[b].y != tag || hi[b].w != tag;
+        const uint32_t w0 = lo[b].x & lo[b].y & lo[b].z & lo[b].w & hi[b].x & hi[b].y & hi[b].z & hi[b].w;
+        const uint32_t w1 = lo[b].x | lo[b].y | lo[b].z | lo[b].w | hi[b].x | hi[b].y | hi[b].z | hi[b].w;
+        return (w0 >> 16) != tag || (w1 >> 16) != tag;
+      };
+      if (stale()) {
+        const uint32_t o = (uint32_t)((src0 + (size_t)c * EPC) * TB);
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (stale()) {
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_sleep(1);
+          lo[b] = coh_b128(rs, o);
+          hi[b] = coh_b128(rs, o + 16);
+          if (__builtin_amdgcn_s_memrealtime() - t0 > sm.spin) {
+            ok = false;
+            break;
+          }
+        }
+      }
+      uint4 v;
+      if (ACT == F32)
+        v = make_uint4(lo[b].x, lo[b].z, hi[b].x, hi[b].z);
+      else
+        v = make_uint4((lo[b].x & 0xFFFFu) | (lo[b].y << 16), (lo[b].z & 0xFFFFu) | (lo[b].w << 16),
+                       (hi[b].x & 0xFFFFu) | (hi[b].y << 16), (hi[b].z & 0xFFFFu) | (hi[b].w << 16));
+      *reinterpret_cast<uint4*>(sm.big + off + (size_t)c * 16) = v;
+    }
+  }
+  return __ballot(!ok) == 0ull;
+}
+
+/* One flow task: down rows h_lo .. h_lo + nr - 1 of the slice (nr <= kFlowRows; the rest repeat
+ * the last row and are not stored) of item `item` against its staged hidden row; y into LDS. */
+constexpr int kFlowRows = 8;
+
+template <int ACT, int FMT>
+__device__ __forceinline__ void flow_task(const Params& p, const Smem& sm, const DownGeo& g,
+                                          const Mat& m, int e, int inter, int item, int h_lo,
+                                          int nr, bool is_shared) {
+  const int lane = threadIdx.x & 63;
+  const size_t vb = row_vbytes(FMT, inter), sb = row_sbytes(FMT, inter);
+  const uint8_t* vr[kFlowRows];
+  const uint8_t* sr[kFlowRows];
+#pragma unroll
+  for (int c = 0; c < kFlowRows; ++c) {
+    const size_t row = (size_t)e * p.H + g.h0 + h_lo + (c < nr ? c : nr - 1);
+    vr[c] = m.down + row * vb;
+    sr[c] = m.down_s ? m.down_s + row * sb : nullptr;
+  }
+  const int r = __builtin_ctz(uniform(sm.umask[item]));
+  const void* arow[1] = {sm.big + (size_t)sm.voff[item][r] * 16};
+  float acc[kFlowRows][1];
+#pragma unroll
+  for (int c = 0; c < kFlowRows; ++c) acc[c][0] = 0.0f;
+  dot_rows<FMT, ACT, 1, kFlowRows, Fmt<FMT>::CH_DN>(vr, sr, inter, arow, 1u, acc);
+  const int slot = is_shared ? p.K : sm.uslot[item][r];
+#pragma unroll
+  for (int c = 0; c < kFlowRows; ++c) {
+    const float t = wave_sum(acc[c][0]);
+    if (lane == 0 && c < nr) g.y[((size_t)(h_lo + c) * p.R + r) * (p.K + 1) + slot] = t;
+  }
+}
+
+/* The down tasks of this wave (no workgroup barrier inside). Returns false when some item's
+ * hidden row did not arrive in time (the caller reports once per workgroup). */
+template <int ACT, int RFMT, int SFMT>
+__device__ __forceinline__ bool ph_down_flow(const Params& p, Smem& sm, uint32_t htag) {
+  const DownGeo g = down_geo(p, sm);
+  const int nU = sm.nU, n_items = nU + (p.Is > 0 ? 1 : 0);
+  const size_t ab = ACT == F32 ? 4 : 2;
+  const int nq = (g.nh + kFlowRows - 1) / kFlowRows, ntask = n_items * nq;
+  bool ok = true;
+  for (;;) {
+    const int d = claim(&sm.down_next);
+    if (d >= ntask) break;
+    const int k = d / nq, q = d % nq, it = down_item(p, sm, k);
+    /* all lanes try; lane 0's attempt is the first, and its old value says who stages */
+    const int st = __builtin_amdgcn_readfirstlane(atomicCAS(&sm.stage_state[k], 0, 1));
+    if (st == 0) {
+      const uint32_t off = flow_off(p, k, ab);
+      const bool got = ok && flow_stage<ACT>(p, sm, it, off, htag);
+      if ((threadIdx.x & 63) == 0) {
+        sm.voff[it][__builtin_ctz(sm.umask[it])] = (uint16_t)(off / 16);
+        __hip_atomic_store(&sm.stage_state[k], got ? 2 : 3, __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      if (!got) ok = false;
+    } else {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      int v;
+      while ((v = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                  &sm.stage_state[k], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP))) == 1) {
+        __builtin_amdgcn_s_sleep(1);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > 4ull * sm.spin) break;
+      }
+      if (v != 2) ok = false;
+    }
+    if (!ok) continue; /* drain the remaining tasks without work */
+    const int h_lo = q * kFlowRows, nr = g.nh - h_lo < kFlowRows ? g.nh - h_lo : kFlowRows;
+    if (it == nU)
+      flow_task<ACT, SFMT>(p, sm, g, p.shared, 0, p.Is, it, h_lo, nr, true);
+    else
+      flow_task<ACT, RFMT>(p, sm, g, p.routed, sm.U[it], p.I, it, h_lo, nr, false);
+  }
+  return ok;
+}
+
 /* Items are processed in groups (down_item order); each group's hidden rows are staged in LDS,
  * then its tasks (item, kRG output rows of the slice) run one per wave. In the fused launch the
  * first group holds at most kFusedGroupItems items and every staging waits (bounded) for the
@@ -1998,21 +2183,7 @@ __device__ __forceinline__ bool ph_down(const Params& p, Smem& sm, uint32_t htag
     k0 = k1;
   }
   __syncthreads();
-  /* combine */
-  for (int q = tid; q < g.nh * R; q += kBlock) {
-    const int hl = q / R, r = q % R;
-    const float* y = g.y + ((size_t)hl * R + r) * (p.K + 1);
-    float routed = 0.0f;
-    for (int j = 0; j < p.K; ++j) routed = fmaf(sm.sel_w[r][j], y[j], routed);
-    const float shared = p.Is > 0 ? act_round<ACT>(y[p.K]) : 0.0f;
-    const float blk = act_round<ACT>(routed + shared);
-    const size_t o = (size_t)r * p.H + g.h0 + hl;
-    if (p.routed_out) p.routed_out[o] = routed;
-    if (p.shared_out) act_st<ACT>(p.shared_out, o, shared);
-    if (p.block) act_st<ACT>(p.block, o, blk);
-    g.blk[q] = blk;
-  }
-  __syncthreads();
+  down_combine<ACT>(p, sm, g);
   return true;
 }
 
@@ -2594,10 +2765,12 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   router_prefetch(p, rpre);
   load_pre_params<ACT>(p, sm);
   load_bias(p, sm);
+  for (int i = threadIdx.x; i <= kMaxUnion; i += kBlock) sm.stage_state[i] = 0;
   if (threadIdx.x == 0) {
     sm.sel_ok = 1;
     sm.shared_next = 0;
     sm.routed_next = 0;
+    sm.down_next = 0;
   }
   __syncthreads();
   stamp(p, tr, 2);
@@ -2642,7 +2815,20 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   if constexpr (RMAX > 1) {
     if (!ph_down_em<ACT, RFMT, SFMT, RMAX>(p, sm, htag)) return;
   } else {
-    if (!ph_down<ACT, RFMT, SFMT, RMAX, true>(p, sm, htag)) return;
+    if (flow_fits(p, sm, ACT == F32 ? 4 : 2)) {
+      const Slice c = slice_of(p);
+      SliceRegs sreg;
+      slice_prefetch<ACT>(p, c, sreg);
+      const bool ok = ph_down_flow<ACT, RFMT, SFMT>(p, sm, htag);
+      if (__syncthreads_or(!ok)) {
+        if (threadIdx.x == 0) report_timeout(p, PH_GATEUP);
+        return;
+      }
+      slice_store(p, c, sm, sreg);
+      down_combine<ACT>(p, sm, down_geo(p, sm));
+    } else if (!ph_down<ACT, RFMT, SFMT, RMAX, true>(p, sm, htag)) {
+      return;
+    }
   }
   stamp(p, tr, 11);
   const DownGeo g = down_geo(p, sm);
