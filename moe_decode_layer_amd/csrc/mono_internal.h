@@ -20,6 +20,7 @@ constexpr int kMaxExperts = 512;
 constexpr int kNMix = 24;            /* 4 pre + 4 post + 16 comb */
 constexpr int kNCarry = kNMix + 1;   /* raw mix sums + sum of squares */
 constexpr int kMixChunk = 256;       /* flattened HC-row elements per mix partial */
+constexpr int kMixGroup = 6;         /* mix outputs per mix-partial task (24 = 4 groups) */
 constexpr int kMaxGrid = 1024;       /* upper bound on persistent workgroups (workspace sizing) */
 constexpr int kLdsActBytes = 114688; /* LDS for the activation rows of the matvec phases */
 constexpr int kLdsHidBytes = 81920;  /* of which: staged SwiGLU hidden rows in the down phase */

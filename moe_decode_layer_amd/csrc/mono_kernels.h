@@ -601,14 +601,16 @@ __device__ __forceinline__ void ph_mix_partials(const Params& p, uint32_t tag, b
   const int n = 4 * p.H, nch = n / kMixChunk;
   const int lane = threadIdx.x & 63;
   const int nwt = gridDim.x * kWaves;
-  /* task = (chunk, row), so each wave reduces 25 sums whatever the number of rows */
-  for (int t = wave_major_id(); t < nch * p.R; t += nwt) {
-    const int ch = t / p.R, r = t % p.R;
+  /* task = (chunk, row, group of kMixGroup outputs; the last group also takes the sum of
+   * squares), so a wave loads kMixGroup weight rows and reduces at most kMixGroup + 1 sums */
+  constexpr int NG = kNMix / kMixGroup;
+  for (int t = wave_major_id(); t < nch * p.R * NG; t += nwt) {
+    const int g = t % NG, ch = t / NG / p.R, r = t / NG % p.R;
     const int base = ch * kMixChunk + lane * 4;
-    float4 w[kNMix];
+    float4 w[kMixGroup];
 #pragma unroll
-    for (int j = 0; j < kNMix; ++j)
-      w[j] = *reinterpret_cast<const float4*>(p.w_mix + (size_t)j * n + base);
+    for (int j = 0; j < kMixGroup; ++j)
+      w[j] = *reinterpret_cast<const float4*>(p.w_mix + (size_t)(g * kMixGroup + j) * n + base);
     float s[4];
     if (ACT == F32) {
       const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(p.state) +
@@ -622,14 +624,16 @@ __device__ __forceinline__ void ph_mix_partials(const Params& p, uint32_t tag, b
     }
     uint64_t* out = p.mix_part + ((size_t)ch * p.R + r) * kNCarry;
 #pragma unroll
-    for (int j = 0; j < kNMix; ++j) {
+    for (int j = 0; j < kMixGroup; ++j) {
       float a = w[j].x * s[0];
       a = fmaf(w[j].y, s[1], a);
       a = fmaf(w[j].z, s[2], a);
       a = fmaf(w[j].w, s[3], a);
       const float tot = wave_sum(a);
-      if (lane == 0 && !skip) st_coh(out + j, ((uint64_t)tag << 32) | __float_as_uint(tot));
+      if (lane == 0 && !skip)
+        st_coh(out + g * kMixGroup + j, ((uint64_t)tag << 32) | __float_as_uint(tot));
     }
+    if (g != NG - 1) continue;
     float ss = s[0] * s[0];
     ss = fmaf(s[1], s[1], ss);
     ss = fmaf(s[2], s[2], ss);
@@ -643,7 +647,7 @@ __device__ __forceinline__ void ph_mix_partials(const Params& p, uint32_t tag, b
  * Prologue of the pre side: hc parameters and the norm weight into LDS (the norm weight sits
  * after the R activation rows in sm.big). */
 template <int ACT>
-__device__ __forceinline__ void load_pre_params(const Params& p, Smem& sm) {
+__device__ __forceinline__ void load_pre_params(const Params& p, Smem& sm, int t0 = 0) {
   const int tid = threadIdx.x;
   if (tid < 3) sm.hcs[tid] = p.hc_scale[tid];
   if (tid < kNMix) sm.hcb[tid] = p.hc_base[tid];
@@ -651,16 +655,22 @@ __device__ __forceinline__ void load_pre_params(const Params& p, Smem& sm) {
   const size_t rows = (size_t)p.R * p.H * ab, wbytes = (size_t)p.H * ab;
   const uint4* s = static_cast<const uint4*>(p.w_norm);
   uint4* d = reinterpret_cast<uint4*>(sm.big + rows);
-  for (size_t i = tid; i < wbytes / 16; i += kBlock) d[i] = s[i];
+  /* the copies run on threads t0 .. kBlock - 1 */
+  const int ct = tid - t0, nt = kBlock - t0;
+  if (ct < 0) {
+    if (tid == 0) sm.state_in_lds = rows + wbytes + 4 * rows <= (size_t)kLdsActBytes ? 1 : 0;
+    return;
+  }
+  for (size_t i = ct; i < wbytes / 16; i += nt) d[i] = s[i];
   /* the state rows too when they fit after the norm weight (one row does: 40 KB at H 5120) */
   const size_t sbytes = 4 * rows;
   const bool fits = rows + wbytes + sbytes <= (size_t)kLdsActBytes;
   if (fits) {
     const uint4* ss = static_cast<const uint4*>(p.state);
     uint4* sd = reinterpret_cast<uint4*>(sm.big + rows + wbytes);
-    for (size_t i = tid; i < sbytes / 16; i += kBlock) sd[i] = ss[i];
+    for (size_t i = ct; i < sbytes / 16; i += nt) sd[i] = ss[i];
   }
-  if (tid == 0) sm.state_in_lds = fits ? 1 : 0;
+  if (ct == 0) sm.state_in_lds = fits ? 1 : 0;
 }
 
 /* Router bias into LDS (read by the select of every workgroup). */
@@ -2758,12 +2768,16 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   /* values exchanged between workgroups carry this launch's tag: no grid barrier */
   const uint32_t tag = (uint32_t)(sm.epoch + 1);
   RouterRegs rpre;
+  int t0 = 0; /* waves below t0 / 64 have a mix-partial task; the others copy the pre inputs */
   if (!p.carry_in) {
+    const int ntask = (4 * p.H / kMixChunk) * p.R * (kNMix / kMixGroup);
+    const int busy = ntask > (int)blockIdx.x ? (ntask - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+    t0 = busy < kWaves ? busy * 64 : 0;
     ph_mix_partials<ACT, RMAX>(p, tag, sm.skip_phase == PH_MIX);
     stamp(p, tr, 1);
   }
   router_prefetch(p, rpre);
-  load_pre_params<ACT>(p, sm);
+  load_pre_params<ACT>(p, sm, t0);
   load_bias(p, sm);
   for (int i = threadIdx.x; i <= kMaxUnion; i += kBlock) sm.stage_state[i] = 0;
   if (threadIdx.x == 0) {
