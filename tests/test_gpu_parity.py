@@ -28,6 +28,10 @@ CASES = {
                                             top_k=16, inter=128, shared_inter=192),
     "bf16_r8_no_shared": C2.with_(rows=8, shared_inter=0, **{k: v for k, v in SMALL.items()
                                                             if k != "shared_inter"}),
+    # one row whose 17 hidden rows (top-16 + shared, 2560 wide) exceed the LDS room of the
+    # one-row down flow, so the fused launch takes the grouped per-slice down phase
+    "bf16_r1_k16_wide": C2.with_(hidden=512, n_experts=64, top_k=16, inter=2560,
+                                 shared_inter=2560),
 }
 
 OUT_KEYS = ["mixes", "pre", "post", "comb", "x", "norm", "logits", "idx", "weights",
