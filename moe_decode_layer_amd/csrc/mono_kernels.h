@@ -1417,10 +1417,158 @@ __device__ __forceinline__ void gateup_task(const Params& p, const Smem& sm, con
   gu_store<ACT, RMAX>(p, sm, acc, i, mask, u, is_shared, htag, hskip);
 }
 
+/* ------------------------------------------------------------------------------------------
+ * Shared-expert gate/up at several rows on the matrix cores. Every row uses the shared expert,
+ * so its gate/up is a small dense product [2 Is x H] x [H x R]. A workgroup takes tiles of 8
+ * hidden rows: 16 weight rows (8 gate, 8 up) against the R activation rows (columns; the 16 - R
+ * spare columns read row 0 and are dropped), with v_mfma_f32_16x16x32_bf16. Its 8 waves split
+ * H into 8 ranges of 32-wide steps and the partial tiles are summed in LDS in wave order.
+ * Operand layout (checked on the device): lane l gives A row l % 16 and B column l % 16, with
+ * k = 32 s + 8 (l / 16) .. + 7; it gets D rows 4 (l / 16) + i, column l % 16. Q8_0 and MXFP4
+ * weights decode exactly to bf16 and their block scale (one per 32-wide step and row)
+ * multiplies each step's product before it is accumulated. */
+typedef __bf16 mfma_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float mfma_f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kMfmaPass = 20; /* steps whose weight loads a wave keeps in flight at once */
+
+__device__ __forceinline__ uint32_t smfma_scratch_off(const Params& p) {
+  return (uint32_t)(((size_t)(p.R + 1) * p.H * 2 + 255) / 256 * 256);
+}
+
+/* The matrix-core path needs bf16 activations, 8-row tiles and its LDS scratch (the partial
+ * tiles of 8 waves and their block scales) after the activation rows and norm weight. */
+template <int ACT>
+__device__ __forceinline__ bool smfma_fits(const Params& p) {
+  return ACT == BF16 && p.R > 1 && p.Is > 0 && p.Is % 8 == 0 &&
+         smfma_scratch_off(p) + 8 * 64 * 16 + 8 * kMfmaPass * 16 * 4 <= (uint32_t)kLdsActBytes;
+}
+
+/* Weight values k .. k + 7 of one row as bf16 (exact), and the row's block scale source. */
+template <int SFMT>
+__device__ __forceinline__ mfma_bf16x8 smfma_a(const uint8_t* row, int k) {
+  mfma_bf16x8 a;
+  if constexpr (SFMT == BF16) {
+    const uint4 v = *reinterpret_cast<const uint4*>(row + (size_t)k * 2);
+    a = __builtin_bit_cast(mfma_bf16x8, v);
+  } else if constexpr (SFMT == Q8) {
+    const uint2 v = *reinterpret_cast<const uint2*>(row + k);
+    const uint32_t d[2] = {v.x, v.y};
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float f0 = (float)(int)(int8_t)d[i];
+      const float f1 = (float)(int)(int8_t)(d[i] >> 8);
+      const float f2 = (float)(int)(int8_t)(d[i] >> 16);
+      const float f3 = (float)(int)(int8_t)(d[i] >> 24);
+      w[2 * i] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+      w[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+    }
+    a = __builtin_bit_cast(mfma_bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  } else {
+    const uint32_t d = *reinterpret_cast<const uint32_t*>(row + k / 2);
+    const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 0));
+    const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 1));
+    const uint32_t w2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 2));
+    const uint32_t w3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 3));
+    a = __builtin_bit_cast(mfma_bf16x8, make_uint4(w0, w1, w2, w3));
+  }
+  return a;
+}
+
+template <int SFMT>
+__device__ __forceinline__ float smfma_scale(const uint8_t* srow, int step) {
+  if constexpr (SFMT == Q8) return f16_to_f32(reinterpret_cast<const uint16_t*>(srow)[step]);
+  else return e8m0_to_f32(srow[step]);
+}
+
+template <int SFMT>
+__device__ __forceinline__ void shared_gu_mfma(const Params& p, Smem& sm, uint32_t htag,
+                                               bool hskip) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int S = p.H / 32, ks0 = wave * S / kWaves, ks1 = (wave + 1) * S / kWaves;
+  const size_t vb = row_vbytes(SFMT, p.H), sb = row_sbytes(SFMT, p.H);
+  float* red = reinterpret_cast<float*>(sm.big + smfma_scratch_off(p)); /* [8][64][4] */
+  float* scl = red + kWaves * 64 * 4; /* [8 waves][kMfmaPass][16 rows] */
+  const int NT = p.Is / 8;
+  const int m = lane % 16, grp = lane / 16;
+  const int n = lane % 16 < p.R ? lane % 16 : 0;
+  const uint16_t* arow = reinterpret_cast<const uint16_t*>(sm.big) + (size_t)n * p.H;
+  for (int tile = blockIdx.x; tile < NT; tile += gridDim.x) {
+    const int i0 = tile * 8;
+    const size_t wr = (size_t)(i0 + (m & 7));
+    const uint8_t* row = (m < 8 ? p.shared.gate : p.shared.up) + wr * vb;
+    mfma_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = ks0; s0 < ks1; s0 += kMfmaPass) {
+      const int ns = ks1 - s0 < kMfmaPass ? ks1 - s0 : kMfmaPass;
+      uint4 a[kMfmaPass];
+#pragma unroll
+      for (int j = 0; j < kMfmaPass; ++j) /* past ns a step repeats the last one, unused */
+        a[j] = __builtin_bit_cast(uint4, smfma_a<SFMT>(row, (s0 + (j < ns ? j : ns - 1)) * 32 + 8 * grp));
+      if constexpr (SFMT != BF16) {
+        /* block scales of the tile's 16 rows for these steps, [step][row] in this wave's LDS */
+        for (int q = lane; q < 16 * ns; q += 64) {
+          const int rr = q % 16, j = q / 16;
+          const uint8_t* srow = (rr < 8 ? p.shared.gate_s : p.shared.up_s) + (size_t)(i0 + (rr & 7)) * sb;
+          scl[(wave * kMfmaPass + j) * 16 + rr] = smfma_scale<SFMT>(srow, s0 + j);
+        }
+        /* the same wave reads them below: its LDS writes complete first */
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+#pragma unroll
+      for (int j = 0; j < kMfmaPass; ++j) {
+        if (j < ns) {
+          const int k = (s0 + j) * 32 + 8 * grp;
+          const mfma_bf16x8 av = __builtin_bit_cast(mfma_bf16x8, a[j]);
+          const mfma_bf16x8 b =
+              __builtin_bit_cast(mfma_bf16x8, *reinterpret_cast<const uint4*>(arow + k));
+          if constexpr (SFMT == BF16) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, acc, 0, 0, 0);
+          } else {
+            const mfma_f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+            const mfma_f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, zero, 0, 0, 0);
+            const float* sc = scl + (wave * kMfmaPass + j) * 16 + 4 * grp;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc[i], t[i], acc[i]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wave * 64 + lane) * 4 + i] = acc[i];
+    __syncthreads();
+    if (wave == 0) {
+      float d[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float t = 0.0f;
+        for (int w = 0; w < kWaves; ++w) t += red[(w * 64 + lane) * 4 + i];
+        d[i] = t;
+      }
+      /* lanes 0-31 hold gate rows 0-7, lanes 32-63 the matching up rows */
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float up = __shfl(d[i], lane + 32);
+        const int rowh = 4 * grp + i, col = lane % 16;
+        if (lane < 32 && col < p.R && !hskip) {
+          const float g = act_round<BF16>(d[i]);
+          const float u = act_round<BF16>(up);
+          const float h = act_round<BF16>(g / (1.0f + expf(-g)) * u);
+          hid_store<BF16>(p.h_shared, (size_t)col * p.Is + i0 + rowh, h, htag);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 /* Shared-expert gate/up: Is tasks spread over compute units first. */
 template <int ACT, int SFMT, int RMAX>
-__device__ __forceinline__ void ph_gateup_shared(const Params& p, const Smem& sm) {
+__device__ __forceinline__ void ph_gateup_shared(const Params& p, Smem& sm) {
   if (p.Is <= 0) return;
+  if (RMAX > 1 && smfma_fits<ACT>(p)) {
+    shared_gu_mfma<SFMT>(p, sm, 0u, false);
+    return;
+  }
   const int nwt = gridDim.x * kWaves;
   const uint32_t mask = (1u << p.R) - 1u;
   for (int i = wave_major_id(); i < p.Is; i += nwt)
@@ -1446,6 +1594,10 @@ template <int ACT, int SFMT, int RMAX>
 __device__ __forceinline__ void ph_gateup_shared_claim(const Params& p, Smem& sm, uint32_t htag,
                                                        bool hskip) {
   if (p.Is <= 0) return;
+  if (RMAX > 1 && smfma_fits<ACT>(p)) {
+    shared_gu_mfma<SFMT>(p, sm, htag, hskip);
+    return;
+  }
   const uint32_t mask = (1u << p.R) - 1u;
   for (;;) {
     const int i = (int)blockIdx.x + claim(&sm.shared_next) * (int)gridDim.x;
