@@ -2424,6 +2424,11 @@ __device__ __forceinline__ void em_down_task(const Params& p, const Smem& sm, co
   em_store<RMAX>(p, sm, acc, mask, item, hb, nr, is_shared, Kp, tag);
 }
 
+template <int NA, int DG>
+__device__ __forceinline__ void dn_store(const Params& p, const Smem& sm, float (&acc)[DG][NA],
+                                         int it, int hb, const int (&rows)[NA], int Kp,
+                                         uint32_t tag);
+
 /* DG down rows from hb of routed item `it` for the NA rows in `mask` (NA = its population),
  * streamed at once against their staged hidden rows; publishes y[r][slot][hb + c]. */
 template <int ACT, int FMT, int NA, int DG>
@@ -2456,16 +2461,96 @@ __device__ __forceinline__ void dn_wide(const Params& p, const Smem& sm, int it,
 #pragma unroll
     for (int a = 0; a < NA; ++a) acc[c][a] = 0.0f;
   dot_rows<FMT, ACT, NA, DG, Fmt<FMT>::CH_DN>(vr, sr, p.I, arow, (1u << NA) - 1u, acc);
+  dn_store<NA, DG>(p, sm, acc, it, hb, rows, Kp, tag);
+}
+
+/* Publishes y[r][slot][hb + c] for the NA rows of item `it` from the per-lane partial sums of
+ * its DG down rows (lane c stores row c: one coalesced store per row). */
+template <int NA, int DG>
+__device__ __forceinline__ void dn_store(const Params& p, const Smem& sm, float (&acc)[DG][NA],
+                                         int it, int hb, const int (&rows)[NA], int Kp,
+                                         uint32_t tag) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int a = 0; a < NA; ++a) {
     const int r = rows[a], slot = sm.uslot[it][r];
+    float v = 0.0f;
 #pragma unroll
     for (int c = 0; c < DG; ++c) {
       const float t = wave_sum(acc[c][a]);
-      if (lane == c)
-        st_coh(p.y_part + ((size_t)r * Kp + slot) * p.H + hb + c,
-               ((uint64_t)tag << 32) | __float_as_uint(t));
+      if (lane == c) v = t;
     }
+    if (lane < DG)
+      st_coh(p.y_part + ((size_t)r * Kp + slot) * p.H + hb + lane,
+             ((uint64_t)tag << 32) | __float_as_uint(v));
+  }
+}
+
+/* Routed down blocks at several rows for Q8_0 and MXFP4 rows that fit one chunk: blocks of
+ * DG / 2 rows, software-pipelined over two register buffers (as the gate/up phase does); loads
+ * past the last block go through an empty resource and read nothing. */
+template <int ACT, int FMT, int RMAX>
+__device__ __forceinline__ void dn_pipelined(const Params& p, Smem& sm, int qa, int qb, int nqi,
+                                             int Kp, uint32_t tag) {
+  constexpr int DGp = Wide<FMT>::DG / 2, CH = Fmt<FMT>::CH_DN;
+  const int lane = threadIdx.x & 63;
+  const size_t vb = row_vbytes(FMT, p.I), sb = row_sbytes(FMT, p.I);
+  /* block q of DG rows = half-blocks 2 q and 2 q + 1 */
+  const int ha = 2 * qa, hbnd = 2 * qb;
+  auto next = [&]() -> int { return ha + claim(&sm.down_next); };
+  auto load = [&](WRegs<FMT, DGp, CH>& W, int t) {
+    const bool live = t < hbnd;
+    const int tt = live ? t : ha;
+    const int it = (tt / 2) / nqi, h0 = ((tt / 2) % nqi) * (2 * DGp) + (tt % 2) * DGp;
+    const int e = sm.U[it];
+#pragma unroll
+    for (int c = 0; c < DGp; ++c) {
+      const size_t row = (size_t)e * p.H + h0 + c;
+      const __amdgpu_buffer_rsrc_t rv = row_rsrc(p.routed.down + row * vb, live ? vb : 0);
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc(p.routed.down_s + row * sb, live ? sb : 0);
+#pragma unroll
+      for (int k = 0; k < CH; ++k) wload<FMT>(rv, rs, k, lane, W.v[c][k], W.sc[c][k]);
+    }
+  };
+  auto compute = [&](const WRegs<FMT, DGp, CH>& W, int t) {
+    const int it = (t / 2) / nqi, h0 = ((t / 2) % nqi) * (2 * DGp) + (t % 2) * DGp;
+    const uint32_t mask = uniform(sm.umask[it]);
+    const int n = __popc(mask);
+    if (n == 1) {
+      const int rows[1] = {__builtin_ctz(mask)};
+      const void* arow[1] = {sm.big + (size_t)sm.voff[it][rows[0]] * 16};
+      float acc[DGp][1];
+#pragma unroll
+      for (int c = 0; c < DGp; ++c) acc[c][0] = 0.0f;
+      wregs_dot<FMT, ACT, 1, DGp, CH>(W, p.I, 0, arow, 1u, acc);
+      dn_store<1, DGp>(p, sm, acc, it, h0, rows, Kp, tag);
+    } else if (n == 2) {
+      const int rows[2] = {__builtin_ctz(mask), __builtin_ctz(mask & (mask - 1u))};
+      const void* arow[2] = {sm.big + (size_t)sm.voff[it][rows[0]] * 16,
+                             sm.big + (size_t)sm.voff[it][rows[1]] * 16};
+      float acc[DGp][2];
+#pragma unroll
+      for (int c = 0; c < DGp; ++c) acc[c][0] = acc[c][1] = 0.0f;
+      wregs_dot<FMT, ACT, 2, DGp, CH>(W, p.I, 0, arow, 3u, acc);
+      dn_store<2, DGp>(p, sm, acc, it, h0, rows, Kp, tag);
+    } else {
+      /* three or more rows (rare): the general loop, which reads its rows again */
+#pragma unroll 1
+      for (int h = h0; h < h0 + DGp; h += kRG)
+        em_down_task<ACT, FMT, RMAX>(p, sm, p.routed, sm.U[it], p.I, it, h, kRG, false, Kp, tag);
+    }
+  };
+  WRegs<FMT, DGp, CH> A, B;
+  int tA = next();
+  load(A, tA);
+  while (tA < hbnd) {
+    const int tB = next();
+    load(B, tB);
+    compute(A, tA);
+    if (tB >= hbnd) break;
+    tA = next();
+    load(A, tA);
+    compute(B, tB);
   }
 }
 
@@ -2477,6 +2562,12 @@ template <int ACT, int FMT, int RMAX>
 __device__ __forceinline__ void em_routed_blocks(const Params& p, Smem& sm, int qa, int qb,
                                                  int nqi, int Kp, uint32_t tag) {
   constexpr int DG = Wide<FMT>::DG;
+  if constexpr (FMT == Q8 || FMT == FP4) {
+    if (p.I <= 64 * Fmt<FMT>::EL * Fmt<FMT>::CH_DN) {
+      dn_pipelined<ACT, FMT, RMAX>(p, sm, qa, qb, nqi, Kp, tag);
+      return;
+    }
+  }
   for (int q = qa + claim(&sm.down_next); q < qb; q = qa + claim(&sm.down_next)) {
     const int it = q / nqi, hb = (q % nqi) * DG;
     const uint32_t mask = uniform(sm.umask[it]);
