@@ -1671,12 +1671,22 @@ __device__ __forceinline__ void gu_wide_store(const Params& p, const Smem& sm,
   }
 }
 
-/* Routed gate/up: workgroup b owns tasks b, b + grid, ... (expert-major order), so at any
- * moment the grid streams one contiguous stretch of rows; its waves claim them one at a time, so
- * a wave that runs ahead takes more and the workgroup's waves end together. At several rows a
+/* Routed gate/up: workgroup b owns one task of every round of grid tasks (expert-major order,
+ * see gu_task), so at any moment the grid streams one contiguous stretch of rows; its waves
+ * claim them one at a time, so a wave that runs ahead takes more and the workgroup's waves end
+ * together. At several rows a
  * task is GB consecutive hidden rows of one expert: when one or two rows use the expert, all
  * 2 GB weight rows stream at once against them; otherwise the rows go one by one for every row
  * that uses the expert. Every hidden value comes from the same per-row dot product either way. */
+/* Task of the n-th routed gate/up claim of this workgroup: round n covers tasks n grid ..
+ * (n + 1) grid - 1 (expert-major, so experts complete in order), and within a round the
+ * workgroup's slot rotates by 37 per round, so one workgroup's rows do not keep the same
+ * address residues (and HBM channels) from round to round. */
+__device__ __forceinline__ int gu_task(int n) {
+  const int G = gridDim.x;
+  return n * G + (int)(((unsigned)blockIdx.x + 37u * (unsigned)n) % (unsigned)G);
+}
+
 /* Routed gate/up at several rows for Q8_0 and MXFP4 rows that fit one chunk: tasks of GB / 2
  * hidden rows, software-pipelined over two register buffers, so a wave issues the loads of its
  * next task before it computes the current one and waits only for the current one's loads
@@ -1689,7 +1699,7 @@ __device__ __forceinline__ void gu_pipelined(const Params& p, Smem& sm, uint32_t
   const int lane = threadIdx.x & 63;
   const int nb = p.I / GBp, T = sm.nU * nb;
   const size_t vb = row_vbytes(FMT, p.H), sb = row_sbytes(FMT, p.H);
-  auto next = [&]() -> int { return (int)blockIdx.x + claim(&sm.routed_next) * (int)gridDim.x; };
+  auto next = [&]() -> int { return gu_task(claim(&sm.routed_next)); };
   auto load = [&](WRegs<FMT, NR, CH>& W, int t) {
     const bool live = t < T;
     const int tt = live ? t : 0;
@@ -1779,7 +1789,7 @@ __device__ __forceinline__ void ph_gateup_routed(const Params& p, Smem& sm, uint
   constexpr int GB = RMAX > 1 ? Wide<RFMT>::GB : 1;
   const int nb = p.I / GB;
   const int T = sm.nU * nb;
-  auto next = [&]() -> int { return (int)blockIdx.x + claim(&sm.routed_next) * (int)gridDim.x; };
+  auto next = [&]() -> int { return gu_task(claim(&sm.routed_next)); };
   for (int t = next(); t < T; t = next()) {
     const int u = t / nb, i0 = (t % nb) * GB;
     const uint32_t mask = uniform(sm.umask[u]);
