@@ -177,8 +177,8 @@ __device__ __forceinline__ bool coh_copy_tagged_to_lds(const uint64_t* src, int 
     uint4 buf[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const int v = v0 + b * kBlock + tid;
-      if (v < npair) buf[b] = coh_b128(r, (uint32_t)v * 16u);
+      const int v = v0 + b * kBlock + tid; /* past the end: a repeated pair, unused */
+      buf[b] = coh_b128(r, (uint32_t)(v < npair ? v : npair - 1) * 16u);
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
@@ -221,8 +221,8 @@ __device__ __forceinline__ void coh_copy_to_lds(const void* src, size_t bytes, u
     uint4 buf[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const int v = v0 + b * kBlock + tid;
-      if (v < n16) buf[b] = coh_b128(r, (uint32_t)v * 16u);
+      const int v = v0 + b * kBlock + tid; /* past the end: a repeated chunk, unused */
+      buf[b] = coh_b128(r, (uint32_t)(v < n16 ? v : n16 - 1) * 16u);
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
@@ -1153,8 +1153,11 @@ __device__ __forceinline__ bool gather_logits(const Params& p, const Smem& sm, i
       for (int h = 0; h < 2; ++h) {
         const int e = lane + 64 * c, q = q0 + h;
         need[c][h] = e < E && q < P;
-        v[c][h] = make_uint2(0u, tag);
-        if (need[c][h]) v[c][h] = coh_b64(lg, (uint32_t)((((size_t)q * p.R + r) * E + e) * 8));
+        /* every load is issued (a valid repeated address when not needed), so all are in
+         * flight together */
+        const int ee = e < E ? e : E - 1, qq = q < P ? q : P - 1;
+        v[c][h] = coh_b64(lg, (uint32_t)((((size_t)qq * p.R + r) * E + ee) * 8));
+        if (!need[c][h]) v[c][h] = make_uint2(0u, tag);
       }
     if (check) {
       auto pending = [&]() {
@@ -2038,8 +2041,12 @@ __device__ __forceinline__ bool stage_copy(const Params& p, Smem& sm, bool check
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int TB = ACT == F32 ? 8 : 4; /* tagged bytes per value */
   constexpr int EPC = ACT == F32 ? 4 : 8; /* values per 16-byte LDS chunk */
-  const __amdgpu_buffer_rsrc_t hr = coh_region(p.h_routed, (size_t)p.R * p.K * p.I * TB);
-  const __amdgpu_buffer_rsrc_t hsr = coh_region(p.h_shared, (size_t)p.R * (p.Is > 0 ? p.Is : 1) * TB);
+  /* one resource over the routed and then the shared hidden rows (consecutive workspace
+   * regions), so every load of a round uses the same scalar resource */
+  const uint8_t* hbase = static_cast<const uint8_t*>(p.h_routed);
+  const uint32_t sh_off = (uint32_t)(static_cast<const uint8_t*>(p.h_shared) - hbase);
+  const __amdgpu_buffer_rsrc_t hr =
+      coh_region(hbase, (size_t)sh_off + (size_t)p.R * (p.Is > 0 ? p.Is : 1) * TB);
   if (threadIdx.x == 0) sm.sel_ok = 1;
   __syncthreads();
   const int nv = sm.nv;
@@ -2053,15 +2060,16 @@ __device__ __forceinline__ bool stage_copy(const Params& p, Smem& sm, bool check
   while (__ballot(v < nv) != 0ull) {
     uint4 lo[B], hi[B];
     uint32_t dst[B], src[B];
+    /* addresses first, then all loads of the round back to back (a lane without a chunk
+     * repeats its first one, unused), then the tag checks */
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       dst[b] = 0xFFFFFFFFu;
+      src[b] = 0u;
       if (v < nv) {
         const uint32_t s0 = sm.vsrc[v];
-        src[b] = ((s0 & ~kHidShared) + (uint32_t)ch * EPC) * TB | (s0 & kHidShared);
-        const __amdgpu_buffer_rsrc_t rs = (s0 & kHidShared) ? hsr : hr;
-        lo[b] = coh_b128(rs, src[b] & ~kHidShared);
-        hi[b] = coh_b128(rs, (src[b] & ~kHidShared) + 16);
+        const uint32_t e0 = s0 & ~kHidShared;
+        src[b] = ((s0 & kHidShared) ? sh_off : 0u) + (e0 + (uint32_t)ch * EPC) * TB;
         dst[b] = (uint32_t)sm.vdst[v] + ch;
         ch += 64;
         while (v < nv && ch >= (int)sm.vlen[v]) {
@@ -2069,6 +2077,12 @@ __device__ __forceinline__ bool stage_copy(const Params& p, Smem& sm, bool check
           ch = lane;
         }
       }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const uint32_t o = dst[b] != 0xFFFFFFFFu ? src[b] : src[0];
+      lo[b] = coh_b128(hr, o);
+      hi[b] = coh_b128(hr, o + 16);
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
@@ -2082,14 +2096,12 @@ __device__ __forceinline__ bool stage_copy(const Params& p, Smem& sm, bool check
           return (w0 >> 16) != tag || (w1 >> 16) != tag;
         };
         if (stale()) {
-          const __amdgpu_buffer_rsrc_t rs = (src[b] & kHidShared) ? hsr : hr;
-          const uint32_t off = src[b] & ~kHidShared;
           const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
           while (stale()) {
             asm volatile("" ::: "memory");
             __builtin_amdgcn_s_sleep(1);
-            lo[b] = coh_b128(rs, off);
-            hi[b] = coh_b128(rs, off + 16);
+            lo[b] = coh_b128(hr, src[b]);
+            hi[b] = coh_b128(hr, src[b] + 16);
             if (__builtin_amdgcn_s_memrealtime() - t0 > sm.spin) {
               ok = false;
               break;
@@ -2178,12 +2190,10 @@ __device__ __forceinline__ bool flow_stage(const Params& p, Smem& sm, int item, 
     uint4 lo[B], hi[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const int c = c0 + b * 64 + lane;
-      const uint32_t o = (uint32_t)((src0 + (size_t)c * EPC) * TB);
-      if (c < nch) {
-        lo[b] = coh_b128(rs, o);
-        hi[b] = coh_b128(rs, o + 16);
-      }
+      const int c = c0 + b * 64 + lane, cc = c < nch ? c : nch - 1; /* cc: unused repeat */
+      const uint32_t o = (uint32_t)((src0 + (size_t)cc * EPC) * TB);
+      lo[b] = coh_b128(rs, o);
+      hi[b] = coh_b128(rs, o + 16);
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
@@ -2610,8 +2620,9 @@ __device__ __forceinline__ bool em_gather_y(const Params& p, Smem& sm, int h0, i
 #pragma unroll
     for (int k = 0; k < B; ++k) {
       const int v = v0 + k * kBlock + tid; /* v = (r Kp + slot) nh + hl */
-      off[k] = (uint32_t)(((size_t)(v / nh) * p.H + h0 + v % nh) * 8);
-      if (v < n) b[k] = coh_b64(yr, off[k]);
+      const int vv = v < n ? v : n - 1; /* past the end: a repeated value, unused */
+      off[k] = (uint32_t)(((size_t)(vv / nh) * p.H + h0 + vv % nh) * 8);
+      b[k] = coh_b64(yr, off[k]);
     }
 #pragma unroll
     for (int k = 0; k < B; ++k) {
