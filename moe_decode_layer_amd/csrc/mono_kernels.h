@@ -4,8 +4,9 @@
  *
  * The layer-half step is written as phases (device functions). The unfused entry points run
  * each phase as its own kernel; the fused entry point runs every phase in ONE persistent launch
- * (one workgroup per compute unit) separated by device-wide barriers. Every output element has
- * a fixed decomposition (one wave per dot product, fixed lane mapping, fixed reduction tree),
+ * (one workgroup per compute unit) with no grid barrier: workgroups hand values to each other
+ * tagged with the launch epoch and the readers poll for the tag. Every output element has a
+ * fixed decomposition (one wave per dot product, fixed lane mapping, fixed reduction tree),
  * independent of which workgroup computes it, so the fused and unfused paths give identical
  * bytes.
  *
@@ -14,12 +15,13 @@
  * (1 KB per wave per step, coalesced), a wave keeps a whole row's loads in flight, weights are
  * decoded once per vector into packed bf16 pairs (exact for bf16, Q8_0 and e2m1 values) and
  * every activation row consumes them with v_dot2_f32_bf16 (exact products, f32 sums).
- * Activations live in LDS. Reductions use DPP. MFMA is not used at these widths.
+ * Activations live in LDS. Reductions use DPP. The one dense product of the step, the shared
+ * expert's gate/up at several rows, runs on the matrix cores (v_mfma_f32_16x16x32_bf16).
  *
- * Data that crosses workgroups inside the fused launch (mix partials, logits, hidden rows,
- * carry partials) is written with device-coherent (sc1) stores and read with device-coherent
- * loads; a barrier is a plain device-scope counter that a workgroup increments only after its
- * stores have completed. No cache write-back or invalidation is needed.
+ * Data that crosses workgroups inside the fused launch (mix partials, logit parts, hidden rows,
+ * down outputs at several rows, carry partials) is written with device-coherent (sc1) stores,
+ * each value with the launch tag beside it, and read with device-coherent loads that poll
+ * until the tag is current. No cache write-back or invalidation is needed.
  *
  * Steps and rounding points follow the ds4 page "v41: fuse the single-box decode glue (HC, MoE,
  * attention)" ("What" and its HC and router/shared-expert commits); the fused launch follows K2
@@ -113,19 +115,6 @@ template <typename T>
 __device__ __forceinline__ void st_coh(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ldf_coh(const float* p) {
-  return __uint_as_float(ld_coh(reinterpret_cast<const uint32_t*>(p)));
-}
-__device__ __forceinline__ void stf_coh(float* p, float v) {
-  st_coh(reinterpret_cast<uint32_t*>(p), __float_as_uint(v));
-}
-template <int ACT>
-__device__ __forceinline__ void act_st_coh(void* p, size_t i, float v) {
-  if (ACT == F32)
-    stf_coh(static_cast<float*>(p) + i, v);
-  else
-    st_coh(static_cast<uint16_t*>(p) + i, (uint16_t)f2bf(v));
-}
 
 /* Tagged hidden-row value: bf16 bits | tag << 16 (uint32) or f32 bits | tag << 32 (uint64). */
 template <int ACT>
@@ -146,9 +135,6 @@ constexpr int kCohPolicy = 16; /* sc1: device scope */
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_region(const void* base, size_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
-}
-__device__ __forceinline__ float coh_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCohPolicy));
 }
 __device__ __forceinline__ uint4 coh_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCohPolicy);
@@ -209,31 +195,6 @@ __device__ __forceinline__ bool coh_copy_tagged_to_lds(const uint64_t* src, int 
 /* Waits until this wave's memory operations have completed (and orders the compiler). */
 __device__ __forceinline__ void drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-/* Copies `bytes` (a multiple of 4) of device-coherent global memory at `src` into LDS at `dst`
- * with the whole workgroup: 16-byte loads, up to 8 per thread in flight before they are stored,
- * then 4-byte loads for a tail. The caller synchronises before reading dst. */
-__device__ __forceinline__ void coh_copy_to_lds(const void* src, size_t bytes, uint8_t* dst) {
-  const int tid = threadIdx.x;
-  const __amdgpu_buffer_rsrc_t r = coh_region(src, bytes);
-  const int n16 = (int)(bytes / 16);
-  constexpr int B = 8;
-  for (int v0 = 0; v0 < n16; v0 += B * kBlock) {
-    uint4 buf[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const int v = v0 + b * kBlock + tid; /* past the end: a repeated chunk, unused */
-      buf[b] = coh_b128(r, (uint32_t)(v < n16 ? v : n16 - 1) * 16u);
-    }
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const int v = v0 + b * kBlock + tid;
-      if (v < n16) reinterpret_cast<uint4*>(dst)[v] = buf[b];
-    }
-  }
-  const int t = n16 * 4 + tid;
-  if (t < (int)(bytes / 4))
-    reinterpret_cast<float*>(dst)[t] = coh_f32(r, (uint32_t)t * 4u);
-}
 
 /* ------------------------------------------------------------------------------------------
  * Wave reductions (DPP butterflies inside each row of 16 lanes, then the four row sums). Must
@@ -922,16 +883,15 @@ __device__ __forceinline__ void act_rows_ptrs(const Params& p, const Smem& sm,
 /* ------------------------------------------------------------------------------------------
  * Phase: router logits [ds4 router commit: the F32 logits matvec]. One wave per expert row,
  * rows spread over compute units first; the fused launch loads each wave's first row before
- * the mix barrier. */
+ * it gathers the mix partials. */
 typedef WRegs<F32, 1, kRouterCh> RouterRegs;
 
-/* Issues the loads of this wave's first router row chunk (task order of ph_router). */
 /* Router task of this wave. A row of H values splits into P parts of kRouterCh steps; when
  * ceil(E / grid) * P <= 7, expert e goes to workgroup e % grid and its parts to waves 1, 2, ...
  * there (the select sums the parts in part order), so every wave holds at most one part in
  * flight.
  * Otherwise (local == false) each wave walks whole rows e = wave_major_id() + n * waves. In the
- * local case wave 0 has no router part, so its barrier polls do not queue behind early loads. */
+ * local case wave 0 has no router part, so its polls do not queue behind early loads. */
 struct RouterTask {
   bool local;
   int P, e, part;
@@ -945,7 +905,7 @@ __device__ __forceinline__ RouterTask router_task(const Params& p) {
   t.local = per * t.P <= kWaves - 1;
   const int wave = threadIdx.x >> 6;
   if (t.local) {
-    /* waves 1.. take the parts; wave 0 (which polls the barriers) loads nothing early */
+    /* waves 1.. take the parts; wave 0 (which polls for the tagged values) loads nothing early */
     const int j = (wave - 1) / t.P;
     t.part = (wave - 1) % t.P;
     t.e = wave > 0 && j < per ? (int)blockIdx.x + j * (int)gridDim.x : p.E;
