@@ -55,3 +55,32 @@ def test_fused_in_place_equals_out_of_place(name):
         support.assert_same(got, ref, keys)
     del g
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_chained_in_place_halves_equal_unfused(name):
+    """Three chained layer halves, each taking the previous carry (so it skips its own mix) and
+    overwriting its input state in place, give the same bytes as the unfused calls chained the
+    same way (covers the carry at several rows and in-place at several rows)."""
+    import torch
+    import support
+    cfg = CASES[name]
+    n = 3
+    g = support.Gpu(cfg, layers=tuple(range(n + 1)))
+    R, H = cfg.rows, cfg.hidden
+    keys = ["mixes", "idx", "weights", "block", "new_state", "carry"]
+    st = g.state(4).clone()
+    st_u = st.clone()
+    carry, carry_u = None, None
+    for l in range(n):
+        wn = g.layers[l + 1]["w_mix"]
+        cout = g.buf(R * 25 * 4)
+        ref = g.unfused(st_u, l, carry_u, wn)
+        got = g.fused(st, l, carry, wn, state_out=st, carry_out=cout)
+        support.assert_same(got, ref, keys)
+        st_u = g.buf(R * 4 * H * g.ab)
+        st_u.copy_(st)
+        carry_u = cout.clone()
+        carry = cout
+    del g
+    torch.cuda.empty_cache()
