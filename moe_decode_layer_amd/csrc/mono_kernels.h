@@ -1463,16 +1463,28 @@ __device__ __forceinline__ void shared_gu_mfma(const Params& p, Smem& sm, uint32
     mfma_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int s0 = ks0; s0 < ks1; s0 += kMfmaPass) {
       const int ns = ks1 - s0 < kMfmaPass ? ks1 - s0 : kMfmaPass;
+      /* block scales of the tile's 16 rows for these steps (lane q: row q % 16, step q / 16),
+       * loaded before the weights so that they reach LDS while the weights are in flight */
+      constexpr int NSC = SFMT != BF16 ? (16 * kMfmaPass + 63) / 64 : 1;
+      float sv[NSC];
+      if constexpr (SFMT != BF16) {
+#pragma unroll
+        for (int t = 0; t < NSC; ++t) {
+          const int q = lane + 64 * t, rr = q % 16, j = q / 16 < ns ? q / 16 : ns - 1;
+          const uint8_t* srow = (rr < 8 ? p.shared.gate_s : p.shared.up_s) + (size_t)(i0 + (rr & 7)) * sb;
+          sv[t] = smfma_scale<SFMT>(srow, s0 + j);
+        }
+      }
       uint4 a[kMfmaPass];
 #pragma unroll
       for (int j = 0; j < kMfmaPass; ++j) /* past ns a step repeats the last one, unused */
         a[j] = __builtin_bit_cast(uint4, smfma_a<SFMT>(row, (s0 + (j < ns ? j : ns - 1)) * 32 + 8 * grp));
       if constexpr (SFMT != BF16) {
-        /* block scales of the tile's 16 rows for these steps, [step][row] in this wave's LDS */
-        for (int q = lane; q < 16 * ns; q += 64) {
-          const int rr = q % 16, j = q / 16;
-          const uint8_t* srow = (rr < 8 ? p.shared.gate_s : p.shared.up_s) + (size_t)(i0 + (rr & 7)) * sb;
-          scl[(wave * kMfmaPass + j) * 16 + rr] = smfma_scale<SFMT>(srow, s0 + j);
+        /* [step][row] in this wave's LDS */
+#pragma unroll
+        for (int t = 0; t < NSC; ++t) {
+          const int q = lane + 64 * t;
+          if (q < 16 * ns) scl[(wave * kMfmaPass + q / 16) * 16 + q % 16] = sv[t];
         }
         /* the same wave reads them below: its LDS writes complete first */
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
