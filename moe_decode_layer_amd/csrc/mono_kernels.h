@@ -147,8 +147,10 @@ __device__ __forceinline__ uint2 coh_b64(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 
 /* Copies n tagged values (value bits | tag << 32, uint64) at src into LDS as floats at dst with
- * the whole workgroup, two values per 16-byte coherent load. With check, a pair whose tags are
- * not yet `tag` is loaded again (bounded by spin ticks); returns false (uniform) on expiry. */
+ * the whole workgroup, two values per 16-byte coherent load, B loads per thread in flight. With
+ * check, a pair whose tags are not yet `tag` is loaded again (bounded by spin ticks); returns
+ * false (uniform) on expiry. */
+template <int B>
 __device__ __forceinline__ bool coh_copy_tagged_to_lds(const uint64_t* src, int n, float* dst,
                                                        bool check, uint32_t tag, uint32_t spin,
                                                        int* flag) {
@@ -158,7 +160,6 @@ __device__ __forceinline__ bool coh_copy_tagged_to_lds(const uint64_t* src, int 
   if (tid == 0) *flag = 1;
   __syncthreads();
   bool ok = true;
-  constexpr int B = 8;
   for (int v0 = 0; v0 < npair; v0 += B * kBlock) {
     uint4 buf[B];
 #pragma unroll
@@ -658,23 +659,27 @@ __device__ __forceinline__ bool ph_hc_pre(const Params& p, Smem& sm, bool write_
    * then one wave per (row, output) sums them, lanes taking chunks t = lane + 64 m */
   float* part = reinterpret_cast<float*>(sm.big); /* free until x is written below */
   if (!p.carry_in) {
-    if (!coh_copy_tagged_to_lds(p.mix_part, nch * R * kNCarry, part, check, tag, sm.spin,
-                                &sm.flag)) {
+    /* one round of loads per thread when it covers every pair (up to 8 rows at H 5120) */
+    const int n = nch * R * kNCarry;
+    const bool got = n <= 2 * 8 * kBlock
+                         ? coh_copy_tagged_to_lds<8>(p.mix_part, n, part, check, tag, sm.spin, &sm.flag)
+                         : coh_copy_tagged_to_lds<16>(p.mix_part, n, part, check, tag, sm.spin, &sm.flag);
+    if (!got) {
       if (threadIdx.x == 0) report_timeout(p, PH_MIX);
       return false;
     }
   }
   __syncthreads();
-  for (int q = wave; q < R * kNCarry; q += kWaves) {
+  /* one thread per (row, output) sums the chunk partials in chunk order */
+  for (int q = tid; q < R * kNCarry; q += kBlock) {
     const int r = q / kNCarry, j = q % kNCarry;
     float v = 0.0f;
     if (p.carry_in) {
-      if (lane == 0) v = p.carry_in[r * kNCarry + j];
+      v = p.carry_in[r * kNCarry + j];
     } else {
-      for (int t = lane; t < nch; t += 64) v += part[((size_t)t * R + r) * kNCarry + j];
+      for (int t = 0; t < nch; ++t) v += part[(size_t)t * R * kNCarry + q];
     }
-    const float tot = wave_sum(v);
-    if (lane == 0) sm.raw[r][j] = tot;
+    sm.raw[r][j] = v;
   }
   __syncthreads();
   stamp(p, sm.trace_on != 0, 14);
