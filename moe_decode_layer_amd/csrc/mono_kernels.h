@@ -477,7 +477,8 @@ struct Smem {
   int trace_on;
   int state_in_lds;
   float bias[kMaxExperts];
-  float wnext[kNMix * 4 * kSliceMax]; /* next mix weights of the slice [24][4][hs] */
+  float wnext[kNMix * 4 * kSliceMax]; /* next mix weights of the slice [24][4][hs]; before
+                                         the down phase, the collapse's sums of squares */
   float sslice[kMaxRows * 4 * kSliceMax]; /* input state of the slice [R][4][hs] */
   float cred[kMaxGrid];                  /* carry reduction: one partial per workgroup */
   uint32_t spin;
@@ -709,89 +710,173 @@ __device__ __forceinline__ bool ph_hc_pre(const Params& p, Smem& sm, bool write_
   }
   __syncthreads();
   stamp(p, sm.trace_on != 0, 16);
-  /* collapse: x = bf16(sum_i pre_i state_i), VE consecutive positions per thread, 16-byte
-   * loads of the four streams; sum of squares of the rounded x */
-  float ss[RMAX];
+  /* collapse: x = bf16(sum_i pre_i state_i), in chunks of VE consecutive positions with
+   * 16-byte loads of the four streams, and the sum of squares of the rounded x */
+  if constexpr (RMAX == 1) {
+    /* one row: one thread per chunk; sums of squares per wave, then in wave order */
+    float ss[RMAX];
 #pragma unroll
-  for (int r = 0; r < RMAX; ++r) ss[r] = 0.0f;
-  constexpr int RB = RMAX < 4 ? RMAX : 4; /* rows whose loads are in flight together */
-  for (int c = tid; c < H / VE; c += kBlock) {
+    for (int r = 0; r < RMAX; ++r) ss[r] = 0.0f;
+    constexpr int RB = 1;
+    for (int c = tid; c < H / VE; c += kBlock) {
 #pragma unroll
-    for (int r0 = 0; r0 < RMAX; r0 += RB) {
-      if (r0 >= R) break;
-      uint4 sv[RB][4];
+      for (int r0 = 0; r0 < RMAX; r0 += RB) {
+        if (r0 >= R) break;
+        uint4 sv[RB][4];
 #pragma unroll
-      for (int rr = 0; rr < RB; ++rr) {
-        if (r0 + rr >= R) break;
-        const uint8_t* sbase = sm.state_in_lds
-                                   ? sm.big + ((size_t)R + 1) * H * ab
-                                   : static_cast<const uint8_t*>(p.state);
-        const uint8_t* base = sbase + ((size_t)(r0 + rr) * n + (size_t)c * VE) * ab;
+        for (int rr = 0; rr < RB; ++rr) {
+          if (r0 + rr >= R) break;
+          const uint8_t* sbase = sm.state_in_lds
+                                     ? sm.big + ((size_t)R + 1) * H * ab
+                                     : static_cast<const uint8_t*>(p.state);
+          const uint8_t* base = sbase + ((size_t)(r0 + rr) * n + (size_t)c * VE) * ab;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sv[rr][i] = *reinterpret_cast<const uint4*>(base + (size_t)i * H * ab);
-      }
+          for (int i = 0; i < 4; ++i)
+            sv[rr][i] = *reinterpret_cast<const uint4*>(base + (size_t)i * H * ab);
+        }
 #pragma unroll
-      for (int rr = 0; rr < RB; ++rr) {
-        const int r = r0 + rr;
-        if (r >= R) break;
-        const float p0 = sm.pre[r][0], p1 = sm.pre[r][1], p2 = sm.pre[r][2], p3 = sm.pre[r][3];
-        const uint32_t a0[4] = {sv[rr][0].x, sv[rr][0].y, sv[rr][0].z, sv[rr][0].w};
-        const uint32_t a1[4] = {sv[rr][1].x, sv[rr][1].y, sv[rr][1].z, sv[rr][1].w};
-        const uint32_t a2[4] = {sv[rr][2].x, sv[rr][2].y, sv[rr][2].z, sv[rr][2].w};
-        const uint32_t a3[4] = {sv[rr][3].x, sv[rr][3].y, sv[rr][3].z, sv[rr][3].w};
-        uint32_t xo[4];
-        float xf[2];
+        for (int rr = 0; rr < RB; ++rr) {
+          const int r = r0 + rr;
+          if (r >= R) break;
+          const float p0 = sm.pre[r][0], p1 = sm.pre[r][1], p2 = sm.pre[r][2], p3 = sm.pre[r][3];
+          const uint32_t a0[4] = {sv[rr][0].x, sv[rr][0].y, sv[rr][0].z, sv[rr][0].w};
+          const uint32_t a1[4] = {sv[rr][1].x, sv[rr][1].y, sv[rr][1].z, sv[rr][1].w};
+          const uint32_t a2[4] = {sv[rr][2].x, sv[rr][2].y, sv[rr][2].z, sv[rr][2].w};
+          const uint32_t a3[4] = {sv[rr][3].x, sv[rr][3].y, sv[rr][3].z, sv[rr][3].w};
+          uint32_t xo[4];
+          float xf[2];
 #pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          float v0, v1, v2, v3;
-          if (ACT == F32) {
-            v0 = __uint_as_float(a0[e]); v1 = __uint_as_float(a1[e]);
-            v2 = __uint_as_float(a2[e]); v3 = __uint_as_float(a3[e]);
-          } else {
-            const int sh = (e & 1) ? 16 : 0;
-            v0 = bf2f((a0[e >> 1] >> sh) & 0xFFFFu); v1 = bf2f((a1[e >> 1] >> sh) & 0xFFFFu);
-            v2 = bf2f((a2[e >> 1] >> sh) & 0xFFFFu); v3 = bf2f((a3[e >> 1] >> sh) & 0xFFFFu);
-          }
-          float a = p0 * v0;
-          a = fmaf(p1, v1, a);
-          a = fmaf(p2, v2, a);
-          a = fmaf(p3, v3, a);
-          if (ACT == F32) {
-            xo[e] = __float_as_uint(a);
-            ss[r] = fmaf(a, a, ss[r]);
-          } else {
-            xf[e & 1] = a;
-            if (e & 1) {
-              const uint32_t pr = f2bf2(xf[0], xf[1]);
-              xo[e >> 1] = pr;
-              const float x0 = bf2f(pr & 0xFFFFu), x1 = bf2f(pr >> 16);
-              ss[r] = fmaf(x0, x0, ss[r]);
-              ss[r] = fmaf(x1, x1, ss[r]);
+          for (int e = 0; e < VE; ++e) {
+            float v0, v1, v2, v3;
+            if (ACT == F32) {
+              v0 = __uint_as_float(a0[e]); v1 = __uint_as_float(a1[e]);
+              v2 = __uint_as_float(a2[e]); v3 = __uint_as_float(a3[e]);
+            } else {
+              const int sh = (e & 1) ? 16 : 0;
+              v0 = bf2f((a0[e >> 1] >> sh) & 0xFFFFu); v1 = bf2f((a1[e >> 1] >> sh) & 0xFFFFu);
+              v2 = bf2f((a2[e >> 1] >> sh) & 0xFFFFu); v3 = bf2f((a3[e >> 1] >> sh) & 0xFFFFu);
+            }
+            float a = p0 * v0;
+            a = fmaf(p1, v1, a);
+            a = fmaf(p2, v2, a);
+            a = fmaf(p3, v3, a);
+            if (ACT == F32) {
+              xo[e] = __float_as_uint(a);
+              ss[r] = fmaf(a, a, ss[r]);
+            } else {
+              xf[e & 1] = a;
+              if (e & 1) {
+                const uint32_t pr = f2bf2(xf[0], xf[1]);
+                xo[e >> 1] = pr;
+                const float x0 = bf2f(pr & 0xFFFFu), x1 = bf2f(pr >> 16);
+                ss[r] = fmaf(x0, x0, ss[r]);
+                ss[r] = fmaf(x1, x1, ss[r]);
+              }
             }
           }
+          const uint4 xv = make_uint4(xo[0], xo[1], xo[2], xo[3]);
+          const size_t byte = ((size_t)r * H + (size_t)c * VE) * ab;
+          *reinterpret_cast<uint4*>(sm.big + byte) = xv;
+          if (write_out && p.x) *reinterpret_cast<uint4*>(static_cast<uint8_t*>(p.x) + byte) = xv;
         }
-        const uint4 xv = make_uint4(xo[0], xo[1], xo[2], xo[3]);
-        const size_t byte = ((size_t)r * H + (size_t)c * VE) * ab;
-        *reinterpret_cast<uint4*>(sm.big + byte) = xv;
-        if (write_out && p.x) *reinterpret_cast<uint4*>(static_cast<uint8_t*>(p.x) + byte) = xv;
       }
     }
-  }
-  stamp(p, sm.trace_on != 0, 17);
+    stamp(p, sm.trace_on != 0, 17);
 #pragma unroll
-  for (int r = 0; r < RMAX; ++r) {
-    if (r >= R) break;
-    const float t = wave_sum(ss[r]);
-    if (lane == 0) sm.red[wave][r] = t;
+    for (int r = 0; r < RMAX; ++r) {
+      if (r >= R) break;
+      const float t = wave_sum(ss[r]);
+      if (lane == 0) sm.red[wave][r] = t;
+    }
+    __syncthreads();
+    if (tid < R) {
+      float t = 0.0f;
+      for (int w = 0; w < kWaves; ++w) t += sm.red[w][tid];
+      sm.rsum[tid] = t;
+    }
+    __syncthreads();
+  } else {
+    /* several rows: kBlock / R threads per row, each taking chunks of its row with CB chunks'
+     * loads in flight at once (every thread has at most two rounds at H 5120); sums of squares
+     * per thread, then per row in thread order */
+    {
+      const int tpr = kBlock / R, r = tid / tpr, lt = tid % tpr, nchunk = H / VE;
+      constexpr int CB = 5;
+      float ss = 0.0f;
+      if (r < R) {
+        const uint8_t* sbase = sm.state_in_lds ? sm.big + ((size_t)R + 1) * H * ab
+                                               : static_cast<const uint8_t*>(p.state);
+        const float p0 = sm.pre[r][0], p1 = sm.pre[r][1], p2 = sm.pre[r][2], p3 = sm.pre[r][3];
+        for (int c0 = lt; c0 < nchunk; c0 += CB * tpr) {
+          uint4 sv[CB][4];
+#pragma unroll
+          for (int b = 0; b < CB; ++b) {
+            const int c = c0 + b * tpr, cc = c < nchunk ? c : nchunk - 1; /* cc: unused repeat */
+            const uint8_t* base = sbase + ((size_t)r * n + (size_t)cc * VE) * ab;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sv[b][i] = *reinterpret_cast<const uint4*>(base + (size_t)i * H * ab);
+          }
+#pragma unroll
+          for (int b = 0; b < CB; ++b) {
+            const int c = c0 + b * tpr;
+            if (c >= nchunk) break;
+            const uint32_t a0[4] = {sv[b][0].x, sv[b][0].y, sv[b][0].z, sv[b][0].w};
+            const uint32_t a1[4] = {sv[b][1].x, sv[b][1].y, sv[b][1].z, sv[b][1].w};
+            const uint32_t a2[4] = {sv[b][2].x, sv[b][2].y, sv[b][2].z, sv[b][2].w};
+            const uint32_t a3[4] = {sv[b][3].x, sv[b][3].y, sv[b][3].z, sv[b][3].w};
+            uint32_t xo[4];
+            float xf[2];
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+              float v0, v1, v2, v3;
+              if (ACT == F32) {
+                v0 = __uint_as_float(a0[e]); v1 = __uint_as_float(a1[e]);
+                v2 = __uint_as_float(a2[e]); v3 = __uint_as_float(a3[e]);
+              } else {
+                const int sh = (e & 1) ? 16 : 0;
+                v0 = bf2f((a0[e >> 1] >> sh) & 0xFFFFu); v1 = bf2f((a1[e >> 1] >> sh) & 0xFFFFu);
+                v2 = bf2f((a2[e >> 1] >> sh) & 0xFFFFu); v3 = bf2f((a3[e >> 1] >> sh) & 0xFFFFu);
+              }
+              float a = p0 * v0;
+              a = fmaf(p1, v1, a);
+              a = fmaf(p2, v2, a);
+              a = fmaf(p3, v3, a);
+              if (ACT == F32) {
+                xo[e] = __float_as_uint(a);
+                ss = fmaf(a, a, ss);
+              } else {
+                xf[e & 1] = a;
+                if (e & 1) {
+                  const uint32_t pr = f2bf2(xf[0], xf[1]);
+                  xo[e >> 1] = pr;
+                  const float x0 = bf2f(pr & 0xFFFFu), x1 = bf2f(pr >> 16);
+                  ss = fmaf(x0, x0, ss);
+                  ss = fmaf(x1, x1, ss);
+                }
+              }
+            }
+            const uint4 xv = make_uint4(xo[0], xo[1], xo[2], xo[3]);
+            const size_t byte = ((size_t)r * H + (size_t)c * VE) * ab;
+            *reinterpret_cast<uint4*>(sm.big + byte) = xv;
+            if (write_out && p.x) *reinterpret_cast<uint4*>(static_cast<uint8_t*>(p.x) + byte) = xv;
+          }
+        }
+      }
+      stamp(p, sm.trace_on != 0, 17);
+      static_assert(kNMix * 4 * kSliceMax >= kBlock, "one sum per thread");
+      float* ssp = sm.wnext; /* free until the slice is loaded for the expand */
+      ssp[tid] = ss;
+      __syncthreads();
+      for (int q = wave; q < R; q += kWaves) {
+        float t = 0.0f;
+        for (int i = lane; i < tpr; i += 64) t += ssp[q * tpr + i];
+        t = wave_sum(t);
+        if (lane == 0) sm.rsum[q] = t;
+      }
+      __syncthreads();
+    }
   }
-  __syncthreads();
-  if (tid < R) {
-    float t = 0.0f;
-    for (int w = 0; w < kWaves; ++w) t += sm.red[w][tid];
-    sm.rsum[tid] = t;
-  }
-  __syncthreads();
   stamp(p, sm.trace_on != 0, 18);
   /* weighted RMSNorm: norm = bf16(x * (1 / sqrt(mean(x^2) + eps)) * w), VE positions per
    * thread */
