@@ -657,30 +657,47 @@ __device__ __forceinline__ bool ph_hc_pre(const Params& p, Smem& sm, bool write_
   const size_t ab = ACT == F32 ? 4 : 2;
   /* raw mix sums: the tagged partials [chunk][row][25] are copied into LDS with contiguous
    * 16-byte coherent loads (in the fused launch once their tags are current: no grid barrier),
-   * then one wave per (row, output) sums them, lanes taking chunks t = lane + 64 m */
+   * then summed per (row, output) */
   float* part = reinterpret_cast<float*>(sm.big); /* free until x is written below */
   if (!p.carry_in) {
     /* one round of loads per thread when it covers every pair (up to 8 rows at H 5120) */
-    const int n = nch * R * kNCarry;
-    const bool got = n <= 2 * 8 * kBlock
-                         ? coh_copy_tagged_to_lds<8>(p.mix_part, n, part, check, tag, sm.spin, &sm.flag)
-                         : coh_copy_tagged_to_lds<16>(p.mix_part, n, part, check, tag, sm.spin, &sm.flag);
+    const int np = nch * R * kNCarry;
+    const bool got =
+        np <= 2 * 8 * kBlock
+            ? coh_copy_tagged_to_lds<8>(p.mix_part, np, part, check, tag, sm.spin, &sm.flag)
+            : coh_copy_tagged_to_lds<16>(p.mix_part, np, part, check, tag, sm.spin, &sm.flag);
     if (!got) {
       if (threadIdx.x == 0) report_timeout(p, PH_MIX);
       return false;
     }
   }
   __syncthreads();
-  /* one thread per (row, output) sums the chunk partials in chunk order */
-  for (int q = tid; q < R * kNCarry; q += kBlock) {
-    const int r = q / kNCarry, j = q % kNCarry;
-    float v = 0.0f;
-    if (p.carry_in) {
-      v = p.carry_in[r * kNCarry + j];
-    } else {
-      for (int t = 0; t < nch; ++t) v += part[(size_t)t * R * kNCarry + q];
+  if constexpr (RMAX == 1) {
+    /* one row: a wave per output, lanes taking chunks t = lane + 64 m */
+    for (int q = wave; q < R * kNCarry; q += kWaves) {
+      const int r = q / kNCarry, j = q % kNCarry;
+      float v = 0.0f;
+      if (p.carry_in) {
+        if (lane == 0) v = p.carry_in[r * kNCarry + j];
+      } else {
+        for (int t = lane; t < nch; t += 64) v += part[((size_t)t * R + r) * kNCarry + j];
+      }
+      const float tot = wave_sum(v);
+      if (lane == 0) sm.raw[r][j] = tot;
     }
-    sm.raw[r][j] = v;
+  } else {
+    /* several rows: a thread per (row, output), summing the chunks in chunk order (the
+     * 150-200 sums run side by side instead of 19-25 wave reductions one after another) */
+    for (int q = tid; q < R * kNCarry; q += kBlock) {
+      const int r = q / kNCarry, j = q % kNCarry;
+      float v = 0.0f;
+      if (p.carry_in) {
+        v = p.carry_in[r * kNCarry + j];
+      } else {
+        for (int t = 0; t < nch; ++t) v += part[(size_t)t * R * kNCarry + q];
+      }
+      sm.raw[r][j] = v;
+    }
   }
   __syncthreads();
   stamp(p, sm.trace_on != 0, 14);
