@@ -3,7 +3,8 @@ calls and of the fused persistent launch against the oracle (tests/support.py ru
 fused launch byte-identical to the unfused calls.
 
 Cases span all weight formats, 1 to 8 rows, several tiles of every phase and ragged tails
-(hidden 576 over 256 workgroups leaves empty slices; inter 96 leaves idle lanes).
+(hidden 576 over 256 workgroups leaves empty slices; inter 96 leaves idle lanes; 7 rows
+leave an idle collapse thread).
 """
 
 import numpy as np
@@ -28,6 +29,11 @@ CASES = {
                                             top_k=16, inter=128, shared_inter=192),
     "bf16_r8_no_shared": C2.with_(rows=8, shared_inter=0, **{k: v for k, v in SMALL.items()
                                                             if k != "shared_inter"}),
+    "bf16_r4": C2.with_(rows=4, **SMALL),
+    # 7 rows: 73 collapse threads per row (one idle), hidden 640 leaves each matrix-core wave
+    # of the shared gate/up 2 or 3 of its 20 steps (the clamped block-scale loads)
+    "q8_r7_h640": C3.with_(rows=7, hidden=640, n_experts=32, top_k=4, inter=256,
+                           shared_inter=256),
     # one row whose 17 hidden rows (top-16 + shared, 2560 wide) exceed the LDS room of the
     # one-row down flow, so the fused launch takes the grouped per-slice down phase
     "bf16_r1_k16_wide": C2.with_(hidden=512, n_experts=64, top_k=16, inter=2560,
