@@ -26,7 +26,6 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
-sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE decode layer steps/s and achieved HBM GB/s (% peak) at 1 and 6 rows"
@@ -55,18 +54,18 @@ def step_bytes(cfg, idx_rows: np.ndarray, carry: bool) -> int:
 class Workload:
     def __init__(self, cfg, copies: int):
         import torch
-        import support
+        from moe_decode_layer_amd import host
         import moe_decode_layer_amd as mono
         import synth.device as sdev
         self.cfg, self.copies = cfg, copies
         t0 = time.time()
         self.layers = [sdev.layer(cfg, l) for l in range(copies)]
-        self.structs = [support.layer_struct(cfg, d) for d in self.layers]
+        self.structs = [host.layer_struct(cfg, d) for d in self.layers]
         self.states = [sdev.state(cfg, s) for s in range(64)]
-        self.shape = support.shape_of(cfg)
+        self.shape = host.shape_of(cfg)
         self.ws = torch.zeros(mono.mono_workspace_bytes(self.shape), dtype=torch.uint8,
                               device="cuda")
-        mono.mono_workspace_init(self.ws, self.shape, support.stream())
+        mono.mono_workspace_init(self.ws, self.shape, host.current_stream())
         ab = 4 if cfg.act == "f32" else 2
         self.out = torch.zeros(cfg.rows * 4 * cfg.hidden * ab, dtype=torch.uint8, device="cuda")
         self.carry = torch.zeros(cfg.rows * 25 * 4, dtype=torch.uint8, device="cuda")
@@ -84,19 +83,19 @@ class Workload:
 
     def launch(self, i: int):
         import moe_decode_layer_amd as mono
-        import support
+        from moe_decode_layer_amd import host
         l = i % self.copies
         nxt = self.layers[(l + 1) % self.copies]["w_mix"]
         mono.mono_ffn_layer(self.shape, self.structs[l], nxt, self.states[i % 64], None, self.out,
-                            self.carry, self.ws, support.stream())
+                            self.carry, self.ws, host.current_stream())
 
     def selection(self, i: int) -> np.ndarray:
         import moe_decode_layer_amd as mono
-        import support
+        from moe_decode_layer_amd import host
         self.launch(i)
         import torch
         torch.cuda.synchronize()
-        return support.ws_tensor(self.shape, self.ws, mono.MONO_T_IDX, np.int32,
+        return host.ws_tensor(self.shape, self.ws, mono.MONO_T_IDX, np.int32,
                                  (self.cfg.rows, self.cfg.top_k))
 
     def run(self, steps: int, warmup: int):
@@ -128,19 +127,19 @@ class ChainWorkload:
 
     def __init__(self, cfg):
         import torch
-        import support
+        from moe_decode_layer_amd import host
         import moe_decode_layer_amd as mono
         import synth.device as sdev
         self.cfg = cfg
         n = cfg.layers
         t0 = time.time()
         self.layers = [sdev.layer(cfg, l) for l in range(n)]
-        self.structs = [support.layer_struct(cfg, d) for d in self.layers]
+        self.structs = [host.layer_struct(cfg, d) for d in self.layers]
         self.states = [sdev.state(cfg, s) for s in range(64)]
-        self.shape = support.shape_of(cfg)
+        self.shape = host.shape_of(cfg)
         self.ws = torch.zeros(mono.mono_workspace_bytes(self.shape), dtype=torch.uint8,
                               device="cuda")
-        mono.mono_workspace_init(self.ws, self.shape, support.stream())
+        mono.mono_workspace_init(self.ws, self.shape, host.current_stream())
         ab = 4 if cfg.act == "f32" else 2
         nb = cfg.rows * 4 * cfg.hidden * ab
         self.bufs = [torch.zeros(nb, dtype=torch.uint8, device="cuda") for _ in range(2)]
@@ -151,7 +150,7 @@ class ChainWorkload:
 
     def step(self, i: int, on_layer=None):
         import moe_decode_layer_amd as mono
-        import support
+        from moe_decode_layer_amd import host
         n = self.cfg.layers
         st = self.states[i % 64]
         carry_in = None
@@ -159,7 +158,7 @@ class ChainWorkload:
             nxt = self.layers[l + 1]["w_mix"] if l + 1 < n else None
             out, cout = self.bufs[l % 2], self.carry[l % 2]
             mono.mono_ffn_layer(self.shape, self.structs[l], nxt, st, carry_in, out,
-                                cout if nxt is not None else None, self.ws, support.stream())
+                                cout if nxt is not None else None, self.ws, host.current_stream())
             if on_layer is not None:
                 on_layer(l)
             st, carry_in = out, cout
@@ -170,7 +169,7 @@ class ChainWorkload:
         next layer (the carry)."""
         import torch
         import moe_decode_layer_amd as mono
-        import support
+        from moe_decode_layer_amd import host
         import synth
         c = self.cfg
         per_routed = synth.expert_bytes(c.routed_fmt, c.inter, c.hidden)
@@ -181,7 +180,7 @@ class ChainWorkload:
 
         def on_layer(l):
             torch.cuda.synchronize()
-            idx = support.ws_tensor(self.shape, self.ws, mono.MONO_T_IDX, np.int32,
+            idx = host.ws_tensor(self.shape, self.ws, mono.MONO_T_IDX, np.int32,
                                     (c.rows, c.top_k))
             b = len(np.unique(idx)) * per_routed + (per_shared if c.shared_inter else 0)
             b += c.n_experts * c.hidden * 4 + c.n_experts * 4 + c.hidden * ab + 3 * 4 + 24 * 4

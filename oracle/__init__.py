@@ -21,16 +21,21 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB = os.path.join(_HERE, "liboracle.so")
+# MONO_ORACLE_LIB names another build of oracle.c (the pin tests run against planted mistakes
+# this way, see tests/test_oracle_mutants.py)
+LIB = os.environ.get("MONO_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 F32, BF16, Q8_0, MXFP4 = 0, 1, 2, 3
 FMT = {"f32": F32, "bf16": BF16, "q8_0": Q8_0, "mxfp4": MXFP4}
 N_MIX = 24
 
 
-def build() -> None:
-    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
-           "-shared", "-o", LIB, os.path.join(_HERE, "oracle.c"), "-lm"]
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+          "-shared"]
+
+
+def build(src: Optional[str] = None, out: Optional[str] = None) -> None:
+    cmd = ["gcc", *CFLAGS, "-o", out or LIB, src or os.path.join(_HERE, "oracle.c"), "-lm"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("oracle build failed:\n" + r.stderr)

@@ -15,7 +15,6 @@ forcing), so one rounding flip upstream does not cascade.
 
 from __future__ import annotations
 
-import ctypes
 from typing import Dict, Optional
 
 import numpy as np
@@ -43,23 +42,8 @@ def as_f32(a, act: str) -> np.ndarray:
     return np.asarray(a, np.float32) if act == "f32" else bf(a)
 
 
-def shape_of(cfg: synth.Config, rows: Optional[int] = None) -> mono.Shape:
-    return mono.make_shape(cfg.rows if rows is None else rows, cfg.hidden, cfg.n_experts,
-                           cfg.top_k, cfg.inter, cfg.shared_inter, cfg.act, cfg.routed_scale,
-                           cfg.sinkhorn_iters, cfg.eps_hc, cfg.eps_norm)
-
-
-def experts_struct(fmt: str, t: Optional[Dict]) -> mono.Experts:
-    if t is None:
-        return mono.make_experts(fmt, None, None, None)
-    return mono.make_experts(fmt, t["gate"], t["up"], t["down"], t.get("gate_s"), t.get("up_s"),
-                             t.get("down_s"))
-
-
-def layer_struct(cfg: synth.Config, d: Dict) -> mono.Layer:
-    return mono.make_layer(d["w_mix"], d["hc_scale"], d["hc_base"], d["w_norm"], d["w_router"],
-                           d["bias"], experts_struct(cfg.routed_fmt, d["routed"]),
-                           experts_struct(cfg.shared_fmt, d["shared"]))
+from moe_decode_layer_amd.host import (experts_struct, hidden_rows, layer_struct,  # noqa: E402,F401
+                                       shape_of, ws_tensor)
 
 
 def stream() -> int:
@@ -71,28 +55,6 @@ def d2h(t, dtype, shape) -> np.ndarray:
         t.detach().cpu().contiguous().view(torch.uint8).numpy()
     n = int(np.prod(shape)) * np.dtype(dtype).itemsize
     return a[:n].view(dtype).reshape(shape).copy()
-
-
-def hidden_rows(shape: mono.Shape, ws, which: int, adt, dims) -> np.ndarray:
-    """Hidden rows (MONO_T_H_ROUTED / MONO_T_H_SHARED) without their tags: each value is stored
-    beside the launch tag (bf16 in the low half of a uint32, f32 in the low half of a uint64)."""
-    if adt == np.uint16:
-        raw = ws_tensor(shape, ws, which, np.uint32, dims)
-        return (raw & 0xFFFF).astype(np.uint16)
-    raw = ws_tensor(shape, ws, which, np.uint64, dims)
-    return (raw & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
-
-
-def ws_tensor(shape: mono.Shape, ws, which: int, dtype, dims) -> np.ndarray:
-    p, n = mono.mono_workspace_tensor(shape, ws, which)
-    buf = np.empty(int(np.prod(dims)), dtype)
-    assert buf.nbytes <= n, (which, buf.nbytes, n)
-    torch.cuda.synchronize()
-    rc = ctypes.CDLL("libamdhip64.so").hipMemcpy(ctypes.c_void_p(buf.ctypes.data),
-                                                  ctypes.c_void_p(p), ctypes.c_size_t(buf.nbytes),
-                                                  2)
-    assert rc == 0, rc
-    return buf.reshape(dims)
 
 
 class Gpu:

@@ -123,3 +123,41 @@ def test_routed_sum_linear_in_scale_and_selection_order_free():
                    h_routed=a["h_routed"], h_shared=a["h_shared"])
     for key in ("routed", "shared", "block"):
         np.testing.assert_array_equal(f[key], a[key])
+
+
+def _golden(name):
+    import os
+    out = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = line.split(":", 1)
+                out[k.strip()] = v.strip()
+    return out
+
+
+@pytest.mark.parametrize("case", ["shared_rounded", "routed_unrounded"])
+def test_block_rounding_points_hand_derived(case):
+    """tests/golden/block_rounding.txt: block = bf16(routed + bf16(shared)) with routed kept in
+    f32, on exact down products (hidden rows given) where each rounding point changes the
+    result bit."""
+    want = int(_golden("block_rounding.txt")[case], 16)
+    H = I = 32
+    s = oracle.make_shape(1, H, 1, 1, I, I, "bf16", 1.0)
+    hr = np.zeros((1, 1, I))
+    hs = np.zeros((1, I))
+    dr = np.zeros((H, I))
+    ds = np.zeros((H, I))
+    if case == "shared_rounded":
+        dr[:, 0], hr[0, 0, 0] = 3 * 2.0 ** -10, 1.0
+        ds[:, 0], ds[:, 1], hs[0, :2] = 1.0, 2.0 ** -9, 1.0
+    else:
+        dr[:, 0], dr[:, 1], hr[0, 0, :2] = 2.0 ** -8, 2.0 ** -16, 1.0
+        ds[:, 0], hs[0, 0] = 1.0, 1.0
+    z = to_bf(np.zeros((I, H)))
+    routed = {0: {"gate": z, "up": z, "down": to_bf(dr)}}
+    shared = {"gate": z, "up": z, "down": to_bf(ds)}
+    m = oracle.moe(s, None, np.array([[0]]), np.array([[1.0]], np.float32), "bf16", routed,
+                   "bf16", shared, h_routed=to_bf(hr), h_shared=to_bf(hs))
+    assert np.all(m["block"][0] == want), hex(int(m["block"][0, 0]))

@@ -263,3 +263,86 @@ def test_carry_identity(ci):
     direct = oracle.mix(s, new, d1["w_mix"])
     via = oracle.mix(s, None, None, carry)
     np.testing.assert_allclose(via, direct, rtol=1e-6, atol=1e-7)
+
+
+# ------------------------------------------------------------- hand-derived fixtures (golden)
+
+GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden")
+
+
+def _golden_lines(name):
+    with open(__import__("os").path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = line.split(":", 1)
+                yield k.strip(), v.split()
+
+
+@pytest.mark.parametrize("iters", [0, 1, 2])
+def test_sinkhorn_steps_match_hand_derivation(iters):
+    """tests/golden/sinkhorn_steps.txt: 0, 1 and 2 row-then-column normalisations of a fixed
+    4x4 matrix, worked out by hand in exact fractions. Pins the step order (columns first
+    would give the transpose) and the iteration count."""
+    from fractions import Fraction
+    want = {int(k): np.array([float(Fraction(f)) for f in v]).reshape(4, 4)
+            for k, v in _golden_lines("sinkhorn_steps.txt")}[iters]
+    A = np.ones((4, 4))
+    A[0, 0] = 2.0
+    base = np.zeros(24, np.float32)
+    base[8:] = np.log(A).astype(np.float32).ravel()
+    s = oracle.make_shape(1, 64, 8, 2, 32, 32, "f32", 1.0, sinkhorn_iters=iters)
+    _, _, comb = oracle.split(s, np.zeros((1, 24), np.float32), np.zeros(3, np.float32), base)
+    # f32 comb against the exact fractions: the log 2 input carries ~2e-9 relative error
+    np.testing.assert_allclose(comb[0], want, rtol=2e-7, atol=0)
+
+
+def test_collapse_pairs_gate_i_with_stream_i():
+    """tests/golden/collapse_pairing.txt: four distinct streams c_i (h + 1) and distinct
+    power-of-two gates; x = 2 (h + 1) exactly (any other pairing of gates and streams gives
+    another multiple)."""
+    g = dict(_golden_lines("collapse_pairing.txt"))
+    pre = np.array([[float(v) for v in g["pre"]]], np.float32)
+    c = [float(v) for v in g["c"]]
+    mult = float(g["x_over_h_plus_1"][0])
+    H = 32
+    s = oracle.make_shape(1, H, 8, 2, 32, 32, "bf16", 1.0)
+    st = to_bf(np.array([[[ci * (h + 1) for h in range(H)] for ci in c]]))
+    x, _ = oracle.collapse_norm(s, st, pre, to_bf(np.ones(H)))
+    np.testing.assert_array_equal(bf(x[0]), mult * (np.arange(H) + 1.0))
+
+
+def test_norm_depends_on_x_only_through_its_bf16_value():
+    """The RMSNorm reads the stored (bf16-rounded) x: collapsing a row whose sum rounds
+    (x = bf16(v + 0.0035 v)) and collapsing the already rounded x with pre = (1, 0, 0, 0)
+    give the same x and therefore the same norm, bit for bit. A mean of squares taken over
+    the unrounded sums would differ by about 0.3 % and flip many norm outputs."""
+    H = 1024
+    s = oracle.make_shape(1, H, 8, 2, 32, 32, "bf16", 1.0)
+    rng = np.random.default_rng(21)
+    v = to_bf(rng.standard_normal(H))
+    w = to_bf(rng.uniform(0.5, 1.5, H))
+    zero = np.zeros(H, np.uint16)
+    st_a = np.stack([v, v, zero, zero])[None]
+    x_a, norm_a = oracle.collapse_norm(s, st_a, np.array([[1.0, 0.0035, 0.0, 0.0]], np.float32), w)
+    assert np.mean(x_a[0] != v) > 0.3          # the sums really round
+    st_b = np.stack([x_a[0], zero, zero, zero])[None]
+    x_b, norm_b = oracle.collapse_norm(s, st_b, np.array([[1.0, 0.0, 0.0, 0.0]], np.float32), w)
+    np.testing.assert_array_equal(x_b, x_a)
+    np.testing.assert_array_equal(norm_b, norm_a)
+
+
+def test_epsilons_closed_form_on_tiny_rows():
+    """A constant row c = 2^-10 (c^2 ~ 0.95e-6, the size of the epsilons): the mix and the
+    RMSNorm both divide by sqrt(c^2 + 1e-6), about 0.7 of what they would without epsilon."""
+    c = 2.0 ** -10
+    s = small_shape(rows=1, act="bf16")
+    st = to_bf(np.full((1, 4, 64), c))
+    W = np.random.default_rng(22).standard_normal((24, 256)).astype(np.float32)
+    got = oracle.mix(s, st, W)[0]
+    want = np.array([c * sum(map(float, W[j])) / np.sqrt(c * c + 1e-6) for j in range(24)])
+    np.testing.assert_allclose(got, want, rtol=2e-7, atol=1e-9)
+    x, norm = oracle.collapse_norm(s, st, np.array([[1.0, 0.0, 0.0, 0.0]], np.float32),
+                                   to_bf(np.ones(64)))
+    assert np.all(bf(x) == c)
+    assert np.all(norm == to_bf(c / np.sqrt(c * c + 1e-6)))   # 0.6987 -> bf16 0x3F33
