@@ -222,20 +222,22 @@ def summarize(res, cfg):
         achieved_gbs_median=float(np.median(gbs)))
 
 
-def cpu_baseline(cfg, budget_s: float, n_inputs: int = 4):
-    """The oracle, timed on the host cores over whole layer-half steps of the same workload.
+def cpu_oracle_rate(cfg, budget_s: float, threads: int, n_inputs: int = 4, cache=None):
+    """The oracle, timed on `threads` host cores over whole layer-half steps of a workload.
 
-    Steps cycle over `n_inputs` seeded input states; the selected experts' weights are
-    generated on the host outside the timed region and kept for later steps."""
+    Steps cycle over `n_inputs` seeded input states until `budget_s` seconds of oracle compute
+    have passed (at least one step); the selected experts' weights are generated on the host
+    outside the timed region and kept for later steps (in `cache`)."""
     import oracle
     import synth
+    oracle.set_threads(threads)
     s = oracle.shape_of(cfg)
     d0, d1 = synth.dense_host(cfg, 0), synth.dense_host(cfg, 1)
     shared = synth.expert_host(cfg, 0, None)
     states = [synth.state_host(cfg, i) for i in range(n_inputs)]
-    cache = {}
+    cache = {} if cache is None else cache
     done, spent = 0, 0.0
-    while spent < budget_s:
+    while spent < budget_s or done == 0:
         st = states[done % n_inputs]
         # routing (timed), then any missing expert weights generated (untimed), then the rest
         t0 = time.perf_counter()
@@ -254,10 +256,27 @@ def cpu_baseline(cfg, budget_s: float, n_inputs: int = 4):
         oracle.expand(s, st, m["block"], post, comb, d1["w_mix"])
         spent += time.perf_counter() - t0
         done += 1
-    return dict(value=done / spent, unit="steps/s", cores=oracle.threads(), kind="oracle",
+    return dict(value=done / spent, unit="steps/s", cores=threads, kind="oracle",
                 sample="%d full layer-half steps of the same workload (%s) cycling over %d "
-                       "seeded inputs, %.1f s of oracle compute; expert weights generated "
-                       "outside the timed region" % (done, cfg.name, n_inputs, spent))
+                       "seeded inputs, %.1f s of oracle compute on %d thread(s); expert weights "
+                       "generated outside the timed region" % (
+                           done, cfg.name, n_inputs, spent, threads))
+
+
+def cpu_baseline(cfg1, cfg6, budget_s: float):
+    """The oracle on all host cores and on one core, for the 1-row and the 6-row workloads.
+    The headline value is all cores at 1 row."""
+    import oracle
+    n_all = oracle.threads()
+    c1, c6 = {}, {}
+    one_row = cpu_oracle_rate(cfg1, budget_s, n_all, cache=c1)
+    one_row["one_core"] = cpu_oracle_rate(cfg1, budget_s, 1, cache=c1)
+    if cfg6 is not None:
+        six = cpu_oracle_rate(cfg6, budget_s, n_all, n_inputs=2, cache=c6)
+        six["one_core"] = cpu_oracle_rate(cfg6, budget_s, 1, n_inputs=2, cache=c6)
+        one_row["rows6"] = six
+    oracle.set_threads(n_all)
+    return one_row
 
 
 # ---- HBM traffic from rocprofv3 counters -------------------------------------------------
@@ -347,7 +366,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--copies", type=int, default=4, help="independent weight copies rotated")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=5.0,
+                    help="seconds of oracle compute per CPU-baseline leg (4 legs)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-rows6", action="store_true", help="skip the 6- and 8-row workloads")
     ap.add_argument("--no-chain", action="store_true", help="skip the 8-layer chain")
@@ -430,7 +450,8 @@ def main():
                                bytes_per_chain=rc["bytes_per_step_mean"])
         del wc
         torch.cuda.empty_cache()
-    cpu = None if args.no_cpu else cpu_baseline(cfg1, args.cpu_budget)
+    cpu = None if args.no_cpu else cpu_baseline(
+        cfg1, None if args.no_rows6 else synth.CONFIGS[3], args.cpu_budget)
 
     line = {
         "metric": METRIC,

@@ -121,15 +121,17 @@ typedef struct {
 /* Bytes of workspace a step of this shape needs (0 if the shape is invalid). */
 size_t mono_workspace_bytes(const mono_shape* shape);
 
-/* Enqueues the initialisation of ws (counters, error word, debug fields, tagged regions). Needed
- * once before first use, after a MONO_E_TIMEOUT, and when the workspace is used for a different
- * shape (the fused launch tags the values it exchanges between workgroups with a launch count;
- * the init clears the tags). */
+/* Enqueues the initialisation of ws (counters, error word, debug fields, tagged regions) as a
+ * kernel (no memset node, so it can be captured). Needed once before first use and when the
+ * workspace is used for a different shape (the fused launch tags the values it exchanges between
+ * workgroups with a launch count; the init clears the tags); it also clears the error word
+ * after a MONO_E_TIMEOUT. */
 mono_status mono_workspace_init(void* ws, const mono_shape* shape, void* stream);
 
 /* Synchronises `stream`, then copies the workspace error word to err[4] (host memory):
- * err[0] = 0 or 1 (a bounded wait expired), err[1] = phase, err[2] = workgroup, err[3] = number
- * of expired waits. Returns MONO_E_TIMEOUT when err[0] != 0. Not for the hot path. */
+ * err[0] = 0 or 1 (a bounded wait expired in some launch since the last init), err[1] = phase,
+ * err[2] = workgroup, err[3] = number of expired waits. Returns MONO_E_TIMEOUT when err[0] != 0.
+ * Not for the hot path. */
 mono_status mono_workspace_poll(const void* ws, uint32_t err[4], void* stream);
 
 /* Test hooks (enqueued on `stream`): spin_limit_ticks bounds every device-side wait in units of
@@ -234,9 +236,15 @@ mono_status mono_hc_expand(const mono_shape* shape, const void* state, const voi
 
 /* The whole layer half as ONE persistent launch [SGLang mono page, K2; lm-sys page, Layer
  * diagram: mix weights and the shared expert load early, routed weights after routing; vLLM
- * GLM-5 page, Details: residual stream carried across per-layer launches]. Phases are
- * separated by device-wide barriers with bounded waits; on expiry the launch ends early and the
- * workspace error word is set (mono_workspace_poll).
+ * GLM-5 page, Details: residual stream carried across per-layer launches, the epoch advanced
+ * once per step]. One workgroup per compute unit, all resident at once (refused with
+ * MONO_E_UNSUPPORTED when the device cannot hold them). There is no grid barrier: a workgroup
+ * hands each value to others with the launch's epoch tag beside it and the reader polls until
+ * the tag is current. The epoch comes from start counters in ws that every workgroup advances
+ * first, so each launch has its own, also after a launch that ended early. Every wait is
+ * bounded: on expiry the launch ends early, its outputs are invalid, and the error word is set
+ * (mono_workspace_poll reports MONO_E_TIMEOUT from then on, until mono_workspace_init clears
+ * it); later launches on the same workspace compute correct results.
  *   state_in [R][4][H] act; carry_in [R][25] or NULL (as in mono_hc_mix_collapse)
  *   state_out [R][4][H] act (may alias state_in); w_mix_next / carry_out as in mono_hc_expand.
  *   All intermediates are kept in ws (mono_workspace_tensor). */

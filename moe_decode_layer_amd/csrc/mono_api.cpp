@@ -155,6 +155,27 @@ int device_grid(Check& c, const mono_shape* s) {
   return g;
 }
 
+/* The fused launch exchanges values between all of its workgroups, so all of them must be
+ * resident at once: one per compute unit needs an occupancy of at least one (its LDS and
+ * registers), read once per device and kernel instantiation. */
+void check_resident(Check& c, const mono_shape* s, int rf, int sf) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return; /* reported by device_grid */
+  static int cached[64][2][4][4][2]; /* occupancy + 1; 0 = not read yet */
+  const int a = s->act == MONO_F32 ? 0 : 1, m = s->rows > 1 ? 1 : 0;
+  int occ;
+  if (dev < 64 && rf >= 0 && rf < 4 && sf >= 0 && sf < 4 && cached[dev][a][rf][sf][m] != 0) {
+    occ = cached[dev][a][rf][sf][m] - 1;
+  } else {
+    occ = max_active_persistent(s->act, rf, sf, s->rows);
+    if (dev < 64 && rf >= 0 && rf < 4 && sf >= 0 && sf < 4) cached[dev][a][rf][sf][m] = occ + 1;
+  }
+  if (occ < 1)
+    c.fail(MONO_E_UNSUPPORTED,
+           "the fused launch needs one resident workgroup per compute unit, device %d holds %d",
+           dev, occ);
+}
+
 Params base_params(const mono_shape* s, const mono_layer* L, void* ws, int grid) {
   Params p = {};
   p.R = s->rows; p.H = s->hidden; p.E = s->n_experts; p.K = s->top_k; p.I = s->inter;
@@ -475,6 +496,8 @@ mono_status mono_ffn_layer(const mono_shape* shape, const mono_layer* layer,
   c.ptr(ws, "ws", 256);
   if (c.code != MONO_OK || shape->rows == 0) return c.done();
   const int grid = device_grid(c, shape);
+  const int rf = layer->routed.fmt, sf = sfmt_of(shape, layer);
+  if (c.code == MONO_OK) check_resident(c, shape, rf, sf);
   if (c.code != MONO_OK) return c.done();
   Params p = base_params(shape, layer, ws, grid);
   const WsLayout W = ws_layout(*shape);
@@ -493,7 +516,6 @@ mono_status mono_ffn_layer(const mono_shape* shape, const mono_layer* layer,
   p.shared_out = b + W.shared;
   p.routed_out = reinterpret_cast<float*>(b + W.routed);
   p.block = b + W.block;
-  const int rf = layer->routed.fmt, sf = sfmt_of(shape, layer);
   mono_status st = enqueue(K_FFN_LAYER, p, shape, rf, sf, grid, stream, "ffn layer");
   if (st == MONO_OK) g_error.clear();
   return st;

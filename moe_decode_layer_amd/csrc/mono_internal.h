@@ -34,14 +34,16 @@ enum {
   CTL_FAULT_PHASE = 18,
   CTL_TRACE = 19,    /* nonzero: the fused launch records per-phase timestamps */
   CTL_XEND64 = 60,   /* uint64 arrival counter of the unfused expand (last-arriver election) */
-  CTL_BAR64 = 64,    /* uint64 counters [phase - 1][8 groups], never reset (only PH_END used) */
-  CTL_WORDS = 128
+  CTL_START64 = 128, /* uint64 launch-start counters of the fused launch, one per group of
+                        workgroups (blockIdx % 8), each in its own 256-byte block */
+  CTL_WORDS = 128 + 8 * 64
 };
+constexpr int kStartStride = 64; /* u32 words between two start counters */
 
 /* Points where the fused launch's workgroups exchange values (reported in the error word and
- * named by fault injection); PH_END also indexes the end counters that give the launch epoch. */
+ * named by fault injection); PH_END is the expand's wait and the carry reduction. */
 enum { PH_MIX = 1, PH_ROUTER = 2, PH_GATEUP = 3, PH_END = 4 };
-constexpr int kBarGroups = 8; /* one end counter per group of workgroups (blockIdx % 8) */
+constexpr int kBarGroups = 8; /* one start counter per group of workgroups (blockIdx % 8) */
 
 struct Mat {
   int fmt;
@@ -184,6 +186,9 @@ enum Kernel {
 };
 int launch(Kernel k, const Params& p, int act, int rfmt, int sfmt, int grid, void* stream);
 int grid_size_for_device(int device);
+/* Workgroups of the fused launch for (act, routed format, shared format, rows > 1) that one
+ * compute unit holds at once (hipOccupancyMaxActiveBlocksPerMultiprocessor), or -1 for a
+ * combination that is not instantiated. */
 int max_active_persistent(int act, int rfmt, int sfmt, int rows);
 
 }  // namespace mono

@@ -2,10 +2,7 @@
 #include "mono_kernels.h"
 
 namespace mono {
-template int launch_fmt<BF16, FP4, BF16, 1>(Kernel, const Params&, int, hipStream_t);
-template int launch_fmt<BF16, FP4, BF16, kMaxRows>(Kernel, const Params&, int, hipStream_t);
-template int launch_fmt<BF16, FP4, Q8, 1>(Kernel, const Params&, int, hipStream_t);
-template int launch_fmt<BF16, FP4, Q8, kMaxRows>(Kernel, const Params&, int, hipStream_t);
-template int launch_fmt<BF16, FP4, FP4, 1>(Kernel, const Params&, int, hipStream_t);
-template int launch_fmt<BF16, FP4, FP4, kMaxRows>(Kernel, const Params&, int, hipStream_t);
+MONO_INSTANTIATE(BF16, FP4, BF16)
+MONO_INSTANTIATE(BF16, FP4, Q8)
+MONO_INSTANTIATE(BF16, FP4, FP4)
 }  // namespace mono

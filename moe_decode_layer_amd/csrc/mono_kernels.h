@@ -489,16 +489,18 @@ struct Smem {
  * Ordering between the workgroups of the fused launch. There is no grid barrier: every value a
  * workgroup publishes for others (mix partials, router logit parts, hidden rows, carry partials)
  * is stored with a tag of the launch beside it, and the reader waits until the tags are
- * current. The tag comes from the launch epoch: each workgroup adds 1 to an end counter (one
- * of 8 groups, by blockIdx % 8) when it finishes, so at the start of a launch the counters hold
- * epoch * (workgroups of the group) and epoch = count / ceil(grid / 8). Waits are bounded: on
- * expiry the error word is set and the workgroup returns (the workspace then needs
- * mono_workspace_init). Fault injection: workgroup fault_wg withholds its values at fault_phase. */
+ * current. The tag comes from the launch epoch: the first thing every workgroup does is add 1
+ * to a start counter (one of 8, by blockIdx % 8) and keep the old value. Group g has
+ * n_g = ceil((grid - g) / 8) workgroups, so every launch advances counter g by exactly n_g, and
+ * since launches on one workspace run one after another (stream order), every workgroup of the
+ * N-th launch reads an old value in [N n_g, (N + 1) n_g): epoch = old / n_g = N, whatever the
+ * order in which the workgroups start or finish, and also after a launch that ended early.
+ * Waits are bounded: on expiry the error word is set and the workgroup returns; the error word
+ * stays set until mono_workspace_init. Fault injection: workgroup fault_wg withholds its values
+ * at fault_phase. */
 
-/* Counter of `group` for `phase` (only PH_END has one). Workgroup w uses group w % 8, so 32
- * (not 256) arrivals contend for one address. */
-__device__ __forceinline__ uint64_t* bar_counter(const Params& p, int phase, int group) {
-  return reinterpret_cast<uint64_t*>(p.ctl + CTL_BAR64) + (phase - 1) * kBarGroups + group;
+__device__ __forceinline__ uint64_t* start_counter(const Params& p, int group) {
+  return reinterpret_cast<uint64_t*>(p.ctl + CTL_START64 + group * kStartStride);
 }
 
 __device__ __forceinline__ void report_timeout(const Params& p, int phase) {
@@ -510,16 +512,16 @@ __device__ __forceinline__ void report_timeout(const Params& p, int phase) {
   atomicAdd(&e[3], 1u);
 }
 
-/* Reads the launch epoch and debug words once per launch (made visible to the workgroup by the
- * next __syncthreads). Every fused launch advances end counter g by exactly
- * n_g = ceil((grid - g) / 8), and no workgroup finishes before every workgroup has started and
- * read the counters (see end_arrive), so at launch start end counter 0 holds epoch * n_0. */
+/* Takes this workgroup's place in the launch (the epoch, above) and reads the debug words, once
+ * per launch (made visible to the workgroup by the next __syncthreads). */
 __device__ __forceinline__ void bar_setup(const Params& p, Smem& sm) {
   if (threadIdx.x == 0) {
+    const uint32_t g = blockIdx.x % kBarGroups;
+    const uint64_t n = ((uint64_t)gridDim.x - g + kBarGroups - 1) / kBarGroups;
+    const uint64_t old = __hip_atomic_fetch_add(start_counter(p, (int)g), (uint64_t)1,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.epoch = old / n;
     sm.trace_on = ld_coh(p.ctl + CTL_TRACE) != 0u;
-    const uint64_t n0 = ((uint64_t)gridDim.x + kBarGroups - 1) / kBarGroups;
-    const uint64_t epoch = ld_coh(bar_counter(p, PH_END, 0)) / n0;
-    sm.epoch = epoch;
     const uint32_t spin = ld_coh(p.ctl + CTL_SPIN);
     const uint32_t fwg = ld_coh(p.ctl + CTL_FAULT_WG), fph = ld_coh(p.ctl + CTL_FAULT_PHASE);
     sm.spin = spin ? spin : kDefaultSpin;
@@ -2872,18 +2874,6 @@ __device__ __forceinline__ bool reduce_carry(const Params& p, Smem& sm, int q, b
   return all;
 }
 
-/* End-of-launch arrival (no data is published by it): advances this workgroup's end counter
- * once per fused launch, which the next launch reads as its epoch. Every workgroup reads the end
- * counters at its start; the persistent grid is co-resident (one workgroup per compute unit,
- * which the tagged waits between workgroups already require), so every workgroup has started,
- * and read them, before any workgroup can finish. */
-__device__ __forceinline__ void end_arrive(const Params& p, Smem& sm) {
-  __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_fetch_add(bar_counter(p, PH_END, blockIdx.x % kBarGroups), (uint64_t)1,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 /* When the new state overwrites the input (state_out == state), no workgroup may store its
  * slice before every workgroup has read the whole input (mix partials and collapse): each
  * workgroup publishes the launch tag in pre_done[wg] after its collapse, and the expand waits
@@ -2949,10 +2939,7 @@ __device__ __forceinline__ void ph_expand(const Params& p, Smem& sm, const float
       }
     }
   }
-  if (p.w_mix_next == nullptr) {
-    if (FUSED) end_arrive(p, sm);
-    return;
-  }
+  if (p.w_mix_next == nullptr) return;
   stamp(p, sm.trace_on != 0, 12);
   __syncthreads();
   /* carry partials of this slice: cp[j][r][hl] = sum_i W_next[j][i H + h] new[r][i] (j < 24),
@@ -2996,7 +2983,6 @@ __device__ __forceinline__ void ph_expand(const Params& p, Smem& sm, const float
            ((uint64_t)tag << 32) | __float_as_uint(t));
   }
   if (FUSED) {
-    end_arrive(p, sm);
     for (int q = blockIdx.x; q < R * kNCarry; q += gridDim.x)
       if (!reduce_carry(p, sm, q, true, tag)) return;
   } else if (arrive_last_single(p, sm)) {
@@ -3211,6 +3197,24 @@ int launch_fmt(Kernel k, const Params& p, int grid, hipStream_t st) {
     default: return (int)hipErrorInvalidValue;
   }
 }
+
+/* Workgroups of the fused launch one compute unit holds at once (its LDS and registers). */
+template <int ACT, int RFMT, int SFMT, int RMAX>
+int occ_fmt() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_ffn_layer<ACT, RFMT, SFMT, RMAX>, kBlock,
+                                                   0) != hipSuccess)
+    return -1;
+  return n;
+}
+
+/* Explicit instantiation of one (activation, routed format, shared format) combination for one
+ * and for several rows (used by the per-format translation units). */
+#define MONO_INSTANTIATE(A, RF, SF)                                                    \
+  template int launch_fmt<A, RF, SF, 1>(Kernel, const Params&, int, hipStream_t);      \
+  template int launch_fmt<A, RF, SF, kMaxRows>(Kernel, const Params&, int, hipStream_t); \
+  template int occ_fmt<A, RF, SF, 1>();                                                \
+  template int occ_fmt<A, RF, SF, kMaxRows>();
 
 }  // namespace mono
 

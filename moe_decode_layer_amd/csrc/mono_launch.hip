@@ -9,7 +9,9 @@ namespace mono {
 
 #define MONO_FMT_EXTERN(A, RF, SF)                                                         \
   extern template int launch_fmt<A, RF, SF, 1>(Kernel, const Params&, int, hipStream_t);   \
-  extern template int launch_fmt<A, RF, SF, kMaxRows>(Kernel, const Params&, int, hipStream_t);
+  extern template int launch_fmt<A, RF, SF, kMaxRows>(Kernel, const Params&, int, hipStream_t); \
+  extern template int occ_fmt<A, RF, SF, 1>();                                              \
+  extern template int occ_fmt<A, RF, SF, kMaxRows>();
 MONO_FMT_EXTERN(F32, F32, F32)
 MONO_FMT_EXTERN(BF16, BF16, BF16)
 MONO_FMT_EXTERN(BF16, BF16, Q8)
@@ -57,7 +59,8 @@ static int launch_act(Kernel k, const Params& p, int rfmt, int sfmt, int grid, h
  * init are never taken as current. */
 __global__ void k_ws_init(uint32_t* ctl, uint64_t* tagged, size_t tag_words) {
   const int t = threadIdx.x;
-  if (blockIdx.x == 0 && t < CTL_WORDS) ctl[t] = (t == CTL_FAULT_WG) ? 0xFFFFFFFFu : 0u;
+  if (blockIdx.x == 0)
+    for (int w = t; w < CTL_WORDS; w += blockDim.x) ctl[w] = (w == CTL_FAULT_WG) ? 0xFFFFFFFFu : 0u;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + t; i < tag_words;
        i += (size_t)gridDim.x * blockDim.x)
     tagged[i] = 0u;
@@ -99,6 +102,29 @@ int launch_debug(uint32_t* ctl, uint32_t spin, uint32_t fwg, uint32_t fph, void*
 int launch_trace(uint32_t* ctl, uint32_t on, void* stream) {
   hipLaunchKernelGGL(k_ws_trace, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), ctl, on);
   return (int)hipGetLastError();
+}
+
+int max_active_persistent(int act, int rfmt, int sfmt, int rows) {
+  const bool one = rows <= 1;
+  if (act == F32) {
+    if (rfmt == F32 && sfmt == F32) return one ? occ_fmt<F32, F32, F32, 1>() : occ_fmt<F32, F32, F32, kMaxRows>();
+    return -1;
+  }
+  if (act != BF16) return -1;
+#define MONO_OCC_CASE(RF, SF)          \
+  if (rfmt == RF && sfmt == SF)         \
+    return one ? occ_fmt<BF16, RF, SF, 1>() : occ_fmt<BF16, RF, SF, kMaxRows>();
+  MONO_OCC_CASE(BF16, BF16)
+  MONO_OCC_CASE(BF16, Q8)
+  MONO_OCC_CASE(BF16, FP4)
+  MONO_OCC_CASE(Q8, BF16)
+  MONO_OCC_CASE(Q8, Q8)
+  MONO_OCC_CASE(Q8, FP4)
+  MONO_OCC_CASE(FP4, BF16)
+  MONO_OCC_CASE(FP4, Q8)
+  MONO_OCC_CASE(FP4, FP4)
+#undef MONO_OCC_CASE
+  return -1;
 }
 
 int grid_size_for_device(int device) {

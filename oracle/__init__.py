@@ -95,12 +95,18 @@ def lib():
                                   ctypes.c_int64]
         L.or_mat_elem.restype = ctypes.c_double
         L.or_threads.restype = ctypes.c_int
+        L.or_set_threads.argtypes = [ctypes.c_int]
+        L.or_set_threads.restype = None
         _lib = L
     return _lib
 
 
 def threads() -> int:
     return int(lib().or_threads())
+
+
+def set_threads(n: int) -> None:
+    lib().or_set_threads(int(n))
 
 
 def _p(a: Optional[np.ndarray]):

@@ -44,6 +44,14 @@ int or_threads(void) {
 #endif
 }
 
+void or_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ---------------------------------------------------------------------------------------------
  * Number formats (exact decodes; f32 -> bf16 rounds to nearest even). */
 

@@ -93,8 +93,9 @@ double or_e8m0_to_f64(uint8_t e);
 /* Element (row, col) of a matrix with k columns, exactly, in f64. */
 double or_mat_elem(const or_mat* m, int64_t k, int64_t row, int64_t col);
 
-/* Number of threads the oracle's parallel loops use. */
+/* Number of threads the oracle's parallel loops use, and a way to set it (n >= 1). */
 int or_threads(void);
+void or_set_threads(int n);
 
 #ifdef __cplusplus
 }

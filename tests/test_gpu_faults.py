@@ -62,3 +62,37 @@ def test_short_limit_without_a_fault_still_completes():
     support.assert_same(out, ref, ["new_state", "carry", "idx"])
     del g
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("rows", [1, 3])
+def test_launch_after_expired_wait_is_correct_without_init(rows):
+    """A launch that ended early leaves stale tagged values behind; the next launch takes a new
+    epoch from the start counters, so it accepts none of them and computes the same bytes as
+    before, while the error word stays set until the next init."""
+    import torch
+    import support
+    import moe_decode_layer_amd as mono
+    cfg = SMALL if rows == 1 else SMALL_R3
+    g = support.Gpu(cfg, layers=(0, 1))
+    st = g.state(2)
+    wn = g.layers[1]["w_mix"]
+    ref = g.fused(st, 0, None, wn)
+    for phase in (PH_MIX, PH_ROUTER, PH_GATEUP):
+        print("withheld at point", phase, "rows", rows, flush=True)
+        mono.mono_workspace_set_debug(g.ws, 200000, 0, phase, support.stream())
+        new = g.buf(cfg.rows * 4 * cfg.hidden * 2)
+        carry = g.buf(cfg.rows * 25 * 4)
+        mono.mono_ffn_layer(g.shape, g.structs[0], wn, st, None, new, carry, g.ws,
+                            support.stream())
+        status, _ = mono.mono_workspace_poll(g.ws, support.stream())
+        assert status == mono.MONO_E_TIMEOUT
+        mono.mono_workspace_set_debug(g.ws, 0, -1, 0, support.stream())
+        out = g.fused(st, 0, None, wn, expect_ok=False)
+        support.assert_same(out, ref, ["mixes", "logits", "idx", "weights", "h_routed", "block",
+                                       "new_state", "carry"])
+        status, _ = mono.mono_workspace_poll(g.ws, support.stream())
+        assert status == mono.MONO_E_TIMEOUT      # reported until the next init
+    mono.mono_workspace_init(g.ws, g.shape, support.stream())
+    assert mono.mono_workspace_poll(g.ws, support.stream())[0] == mono.MONO_OK
+    del g
+    torch.cuda.empty_cache()

@@ -39,9 +39,14 @@ def test_full_size_layer(ci):
     support.assert_same(fused, unfused, [k for k in OUT_KEYS if k in fused and k in unfused])
     d0, shared = _host(cfg, 0)
     d1 = synth.dense_host(cfg, 1)
+    support.set_case("full-size workload %d" % ci)
     rep = support.compare_stagewise(cfg, fused, synth.state_host(cfg, 5), d0,
                                     lambda e: synth.expert_host(cfg, 0, e), shared, d1["w_mix"])
     print(ci, rep, flush=True)
+    support.set_case("full-size workload %d end-to-end" % ci)
+    e2e = support.compare_end_to_end(cfg, fused, synth.state_host(cfg, 5), d0,
+                                     lambda e: synth.expert_host(cfg, 0, e), shared, d1["w_mix"])
+    print(ci, "end-to-end", {k: v for k, v in e2e.items() if k != "ref"}, flush=True)
     if ci == 4:
         grp = int(np.argmax(d0["bias"][::32]))
         assert fused["idx"][7].tolist() == list(range(32 * grp, 32 * grp + cfg.top_k))
@@ -76,8 +81,21 @@ def test_chain_of_eight_layers_with_carry():
         support.assert_same(outs[l], u, [k for k in OUT_KEYS if k in u and k in outs[l]])
         st_u = states[l + 1]
         carry_u = carries[l + 1]
+    # free running inside each layer: the oracle runs the whole layer half from the GPU's input
+    # state (and carry) of that layer, with no stage forced
+    for l in range(n):
+        d, shared = _host(cfg, l)
+        wn_h = synth.dense_host(cfg, l + 1)["w_mix"] if l + 1 < n else None
+        st_h = support.d2h(states[l], g.adt, (R, 4, H))
+        carry_h = support.d2h(carries[l], np.float32, (R, 25)) if carries[l] is not None else None
+        support.set_case("chain layer %d end-to-end" % l)
+        e2e = support.compare_end_to_end(cfg, outs[l], st_h, d,
+                                         lambda e: synth.expert_host(cfg, l, e), shared, wn_h,
+                                         carry_in=carry_h)
+        print("layer", l, "end-to-end", {k: v for k, v in e2e.items() if k != "ref"}, flush=True)
     # teacher forcing: layer l against the oracle fed the GPU's state and carry of layer l
     for l in range(n):
+        support.set_case("chain layer %d" % l)
         d, shared = _host(cfg, l)
         wn_h = synth.dense_host(cfg, l + 1)["w_mix"] if l + 1 < n else None
         st_h = support.d2h(states[l], g.adt, (R, 4, H))

@@ -25,22 +25,10 @@ def to_bf(x):
 
 
 def dequant(fmt, v, s):
-    """Independent decode of a [rows][k] matrix to f64."""
-    if fmt == "f32":
-        return v.astype(np.float64)
-    if fmt == "bf16":
-        return bf(v).astype(np.float64)
-    if fmt == "q8_0":
-        d = s.view(np.float16).astype(np.float64)
-        return v.astype(np.float64) * np.repeat(d, 32, axis=1)
-    if fmt == "mxfp4":
-        lo, hi = v & 0xF, v >> 4
-        codes = np.stack([lo, hi], axis=-1).reshape(v.shape[0], -1).astype(np.int64)
-        e, m = (codes >> 1) & 3, codes & 1
-        mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0, e - 1) * (1 + m / 2))
-        val = np.where(codes & 8, -mag, mag)
-        return val * np.repeat(np.ldexp(1.0, s.astype(np.int64) - 127), 32, axis=1)
-    raise ValueError(fmt)
+    """Independent decode of a [rows][k] matrix to f64 (numpy's fp16, the E2M1 bit-field
+    formula, ldexp for E8M0)."""
+    import support
+    return support.dequant(fmt, v, s)
 
 
 def silu(x):
