@@ -252,6 +252,23 @@ mono_status mono_ffn_layer(const mono_shape* shape, const mono_layer* layer,
                            const float* w_mix_next, const void* state_in, const float* carry_in,
                            void* state_out, float* carry_out, void* ws, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * For callers that cannot allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): mono_ffn_layer with its workspace in a static device array of
+ * MONO_STATIC_WS_BYTES on each GPU, held from the first call on that GPU until the process
+ * ends. The caller still passes inputs and outputs (as for mono_ffn_layer); the call itself
+ * allocates nothing. The first call on a device, and a call whose shape differs from the previous
+ * call's on that device, first enqueues the workspace initialisation (a kernel) on `stream`.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race. Device-side wait timeouts are recorded in the array's error word, which
+ * this variant does not report. Returns MONO_E_UNSUPPORTED (before any device work) when the
+ * shape's workspace (mono_workspace_bytes) exceeds MONO_STATIC_WS_BYTES. */
+#define MONO_STATIC_WS_BYTES (8u << 20)
+mono_status mono_ffn_layer_static(const mono_shape* shape, const mono_layer* layer,
+                                  const float* w_mix_next, const void* state_in,
+                                  const float* carry_in, void* state_out, float* carry_out,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

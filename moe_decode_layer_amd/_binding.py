@@ -25,7 +25,8 @@ MONO_OK, MONO_E_INVAL, MONO_E_UNSUPPORTED, MONO_E_DEVICE, MONO_E_TIMEOUT = 0, -1
 EXPORTS = ("mono_workspace_bytes", "mono_workspace_init", "mono_workspace_poll",
            "mono_workspace_set_debug", "mono_workspace_set_trace", "mono_workspace_tensor", "mono_last_error",
            "mono_grid_size", "mono_hc_mix_collapse", "mono_router_select", "mono_moe_experts",
-           "mono_hc_expand", "mono_ffn_layer")
+           "mono_hc_expand", "mono_ffn_layer", "mono_ffn_layer_static")
+MONO_STATIC_WS_BYTES = 8 << 20
 
 
 class MonoError(RuntimeError):
@@ -84,6 +85,7 @@ def lib() -> ctypes.CDLL:
             "mono_moe_experts": (I, [SP, P, P, P, LP, P, P, P, P, P]),
             "mono_hc_expand": (I, [SP, P, P, P, P, P, P, P, P, P]),
             "mono_ffn_layer": (I, [SP, LP, P, P, P, P, P, P, P]),
+            "mono_ffn_layer_static": (I, [SP, LP, P, P, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -201,3 +203,10 @@ def mono_ffn_layer(shape, layer, w_mix_next, state_in, carry_in, state_out, carr
     _ok(lib().mono_ffn_layer(ctypes.byref(shape), ctypes.byref(layer), ptr(w_mix_next),
                              ptr(state_in), ptr(carry_in), ptr(state_out), ptr(carry_out),
                              ptr(ws), stream))
+
+
+def mono_ffn_layer_static(shape, layer, w_mix_next, state_in, carry_in, state_out, carry_out,
+                          stream=None) -> None:
+    _ok(lib().mono_ffn_layer_static(ctypes.byref(shape), ctypes.byref(layer), ptr(w_mix_next),
+                                    ptr(state_in), ptr(carry_in), ptr(state_out), ptr(carry_out),
+                                    stream))

@@ -22,11 +22,22 @@ int launch_debug(uint32_t* ctl, uint32_t spin, uint32_t fwg, uint32_t fph, void*
 int launch_trace(uint32_t* ctl, uint32_t on, void* stream);
 }
 
+namespace {
+thread_local std::string g_error;
+}  // namespace
+
+void mono::set_last_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+}
+
 using namespace mono;
 
 namespace {
-
-thread_local std::string g_error;
 
 struct Check {
   std::string msg;

@@ -185,6 +185,8 @@ enum Kernel {
   K_WS_DEBUG
 };
 int launch(Kernel k, const Params& p, int act, int rfmt, int sfmt, int grid, void* stream);
+/* Sets the thread's mono_last_error() text (printf format). */
+void set_last_error(const char* fmt, ...);
 int grid_size_for_device(int device);
 /* Workgroups of the fused launch for (act, routed format, shared format, rows > 1) that one
  * compute unit holds at once (hipOccupancyMaxActiveBlocksPerMultiprocessor), or -1 for a

@@ -152,3 +152,14 @@ def test_workspace_tensor_offsets_stay_inside_the_workspace():
     for which in range(B.MONO_T_TRACE + 1):
         p, n = B.mono_workspace_tensor(s, P256, which)
         assert p >= P256 and p + n <= P256 + total, which
+
+
+def test_static_workspace_refuses_shapes_beyond_its_size():
+    """mono_ffn_layer_static checks the shape's workspace size on the host before any device
+    work: 8 rows with top-16 need more than MONO_STATIC_WS_BYTES."""
+    s = shape(rows=8, top_k=16)
+    assert B.mono_workspace_bytes(s) > B.MONO_STATIC_WS_BYTES
+    with pytest.raises(B.MonoError) as e:
+        B.mono_ffn_layer_static(s, layer(), None, P16, None, P16, None)
+    assert e.value.status == B.MONO_E_UNSUPPORTED
+    assert "static workspace" in e.value.message
