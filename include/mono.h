@@ -137,7 +137,7 @@ mono_status mono_workspace_poll(const void* ws, uint32_t err[4], void* stream);
 /* Test hooks (enqueued on `stream`): spin_limit_ticks bounds every device-side wait in units of
  * the 100 MHz real-time counter (0 = default, 2 s); fault_wg / fault_phase make that workgroup
  * withhold the values it publishes for the other workgroups at that point (-1 = off): 1 its mix
- * partial sums, 2 its router logit parts, 3 its hidden rows. */
+ * partial sums, 2 its router logits, 3 its hidden rows. */
 mono_status mono_workspace_set_debug(void* ws, uint32_t spin_limit_ticks, int32_t fault_wg,
                                      int32_t fault_phase, void* stream);
 

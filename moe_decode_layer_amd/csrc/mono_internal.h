@@ -102,7 +102,7 @@ struct Params {
   uint64_t* pre_done; /* [grid] launch tag of each workgroup once it has read all of the state */
   uint64_t* y_part;   /* [R][Kp][H] tagged down-projection outputs, Kp = K + (shared expert ? 1
                        * : 0), slot K the shared expert */
-  uint64_t* lgp;     /* [parts][R][E] tagged router logit parts (same format) */
+  uint64_t* lgp;     /* [R][E] tagged router logits (same format) */
   uint64_t* trace;   /* [grid][32] real-time stamps */
   size_t tag_words; /* u64 words from carry_part through lgp cleared by the workspace init */
   uint32_t* ctl;
@@ -116,16 +116,8 @@ struct WsLayout {
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-/* The router splits each f32 row of H values into parts of kRouterCh steps of 256 values; the
- * parts are computed by different waves and summed by the select in part order. */
-constexpr int kRouterCh = 10;
-#if defined(__HIPCC__)
-__host__ __device__
-#endif
-inline size_t router_parts(size_t H) {
-  const size_t steps = (H + 255) / 256;
-  return (steps + kRouterCh - 1) / kRouterCh;
-}
+/* Router steps (of 256 f32 values) a wave holds in registers at once. */
+constexpr int kRouterCh = 4;
 
 /* Phase timestamps per workgroup in the trace region. */
 constexpr int kTraceSlots = 32;
@@ -147,7 +139,7 @@ inline WsLayout ws_layout(const mono_shape& s) {
   L.pre_done = take((size_t)kMaxGrid * 8);
   L.y_part = take(R * (k + 1) * H * 8);
   L.mix_part = take(nchunk * R * kNCarry * 8);
-  L.lgp = take(router_parts(s.hidden) * R * E * 8);
+  L.lgp = take(R * E * 8);
   /* hidden rows, tagged: each value with the launch tag beside it (bf16 | tag16 << 16 in a
    * uint32, or f32 | tag32 << 32 in a uint64) */
   L.h_routed = take(R * k * I * ab * 2);

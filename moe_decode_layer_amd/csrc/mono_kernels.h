@@ -18,7 +18,7 @@
  * Activations live in LDS. Reductions use DPP. The one dense product of the step, the shared
  * expert's gate/up at several rows, runs on the matrix cores (v_mfma_f32_16x16x32_bf16).
  *
- * Data that crosses workgroups inside the fused launch (mix partials, logit parts, hidden rows,
+ * Data that crosses workgroups inside the fused launch (mix partials, router logits, hidden rows,
  * down outputs at several rows, carry partials) is written with device-coherent (sc1) stores,
  * each value with the launch tag beside it, and read with device-coherent loads that poll
  * until the tag is current. No cache write-back or invalidation is needed.
@@ -487,7 +487,7 @@ struct Smem {
 
 /* ------------------------------------------------------------------------------------------
  * Ordering between the workgroups of the fused launch. There is no grid barrier: every value a
- * workgroup publishes for others (mix partials, router logit parts, hidden rows, carry partials)
+ * workgroup publishes for others (mix partials, router logits, hidden rows, carry partials)
  * is stored with a tag of the launch beside it, and the reader waits until the tags are
  * current. The tag comes from the launch epoch: the first thing every workgroup does is add 1
  * to a start counter (one of 8, by blockIdx % 8) and keep the old value. Group g has
@@ -545,8 +545,8 @@ __device__ __forceinline__ bool arrive_last_single(const Params& p, Smem& sm) {
   return sm.flag != 0;
 }
 
-__device__ __forceinline__ void stamp(const Params& p, bool on, int slot) {
-  if (on && threadIdx.x == 0)
+__device__ __forceinline__ void stamp(const Params& p, bool on, int slot, int thread = 0) {
+  if (on && (int)threadIdx.x == thread)
     p.trace[(size_t)blockIdx.x * kTraceSlots + slot] = __builtin_amdgcn_s_memrealtime();
 }
 
@@ -636,6 +636,24 @@ __device__ __forceinline__ void load_pre_params(const Params& p, Smem& sm, int t
     for (size_t i = ct; i < sbytes / 16; i += nt) sd[i] = ss[i];
   }
   if (ct == 0) sm.state_in_lds = fits ? 1 : 0;
+}
+
+/* When the state rows do not fit in LDS, the collapse of every workgroup reads the whole state
+ * from memory. While the mix partials of the other workgroups are still on their way, each
+ * workgroup touches its 1/32 share of the state (its rank among the workgroups w with the same
+ * w % 8, which run on one XCD and share its L2), so that the collapse finds the state in L2. */
+template <int ACT>
+__device__ __forceinline__ void warm_state(const Params& p, const Smem& sm) {
+  if (sm.state_in_lds) return;
+  const size_t n16 = (size_t)p.R * 4 * p.H * (ACT == F32 ? 4 : 2) / 16;
+  const int ranks = ((int)gridDim.x + kBarGroups - 1) / kBarGroups;
+  const int rank = (int)blockIdx.x / kBarGroups;
+  const size_t per = (n16 + ranks - 1) / ranks, i0 = rank * per;
+  const size_t i1 = i0 + per < n16 ? i0 + per : n16;
+  uint32_t acc = 0;
+  for (size_t i = i0 + threadIdx.x; i < i1; i += kBlock)
+    acc ^= static_cast<const uint4*>(p.state)[i].x;
+  asm volatile("" ::"v"(acc)); /* the loads are issued and complete here; the value is unused */
 }
 
 /* Router bias into LDS (read by the select of every workgroup). */
@@ -995,62 +1013,73 @@ __device__ __forceinline__ void act_rows_ptrs(const Params& p, const Smem& sm,
  * it gathers the mix partials. */
 typedef WRegs<F32, 1, kRouterCh> RouterRegs;
 
-/* Router task of this wave. A row of H values splits into P parts of kRouterCh steps; when
- * ceil(E / grid) * P <= 7, expert e goes to workgroup e % grid and its parts to waves 1, 2, ...
- * there (the select sums the parts in part order), so every wave holds at most one part in
- * flight.
- * Otherwise (local == false) each wave walks whole rows e = wave_major_id() + n * waves. In the
- * local case wave 0 has no router part, so its polls do not queue behind early loads. */
+/* Router task of this wave. A row of H values has nsteps steps of 256 values. When
+ * ceil(E / grid) <= 7 and each expert's steps fit kRouterCh per wave over its share of the
+ * waves 1 .. 7, expert e goes to workgroup e % grid and its steps are spread over those waves
+ * (local): every wave adds up its steps, the workgroup sums the wave parts in wave order and
+ * stores one tagged logit per (row, expert). Otherwise each wave walks whole rows
+ * e = wave_major_id() + n * waves in chunks of kRouterCh steps. In the local case wave 0 has no
+ * steps, so its polls do not queue behind early loads. */
 struct RouterTask {
   bool local;
-  int P, e, part;
+  int per, nw; /* local: experts per workgroup, waves per expert */
+  int e, s0, cnt;
 };
 
 __device__ __forceinline__ RouterTask router_task(const Params& p) {
   RouterTask t;
   const int nsteps = (p.H + 255) / 256;
-  t.P = (nsteps + kRouterCh - 1) / kRouterCh;
-  const int per = (p.E + (int)gridDim.x - 1) / (int)gridDim.x;
-  t.local = per * t.P <= kWaves - 1;
+  t.per = (p.E + (int)gridDim.x - 1) / (int)gridDim.x;
+  t.nw = t.per <= kWaves - 1 ? (kWaves - 1) / t.per : 1;
+  const int spw = (nsteps + t.nw - 1) / t.nw;
+  t.local = t.per <= kWaves - 1 && spw <= kRouterCh;
   const int wave = threadIdx.x >> 6;
   if (t.local) {
-    /* waves 1.. take the parts; wave 0 (which polls for the tagged values) loads nothing early */
-    const int j = (wave - 1) / t.P;
-    t.part = (wave - 1) % t.P;
-    t.e = wave > 0 && j < per ? (int)blockIdx.x + j * (int)gridDim.x : p.E;
+    const int j = (wave - 1) / t.nw, sub = (wave - 1) % t.nw;
+    t.e = wave > 0 && j < t.per ? (int)blockIdx.x + j * (int)gridDim.x : p.E;
+    t.s0 = wave > 0 ? sub * spw : 0;
+    t.cnt = wave > 0 ? max(0, min(spw, nsteps - t.s0)) : 0;
   } else {
-    t.part = 0;
     t.e = wave_major_id();
+    t.s0 = 0;
+    t.cnt = min(kRouterCh, nsteps);
   }
   return t;
+}
+
+/* Loads steps s0 .. s0 + cnt - 1 (cnt <= kRouterCh) of f32 router row e; the other registers
+ * are zero. */
+__device__ __forceinline__ void router_load(const Params& p, int e, int s0, int cnt, RouterRegs& W) {
+  const int lane = threadIdx.x & 63;
+  const uint4* row = reinterpret_cast<const uint4*>(p.w_router + (size_t)e * p.H);
+#pragma unroll
+  for (int c = 0; c < kRouterCh; ++c) {
+    const int q = (s0 + c) * 64 + lane; /* 16-byte unit: f32 values 4 q .. 4 q + 3 */
+    W.v[0][c] = c < cnt && q * 4 < p.H ? row[q] : make_uint4(0, 0, 0, 0);
+    W.sc[0][c] = 0;
+  }
 }
 
 /* Issues the loads of this wave's first router chunk (the task order of ph_router). */
 __device__ __forceinline__ void router_prefetch(const Params& p, RouterRegs& W) {
   const RouterTask t = router_task(p);
-  if (t.e < p.E) {
-    const uint8_t* vr[1] = {reinterpret_cast<const uint8_t*>(p.w_router + (size_t)t.e * p.H)};
-    const uint8_t* sr[1] = {nullptr};
-    wregs_load(W, vr, sr, p.H, t.part * kRouterCh);
-  }
+  if (t.e < p.E) router_load(p, t.e, t.s0, t.cnt, W);
 }
 
-/* acc[r] += kRouterCh steps of one f32 router row (in W, from step s0) . act row r. */
+/* acc[r] += steps s0 .. s0 + cnt - 1 of one f32 router row (in W) . act row r. Values past H
+ * are zero in W and read a valid act address. */
 template <int ACT, int RMAX>
-__device__ __forceinline__ void router_dot(const RouterRegs& W, int s0, int H, bool whole,
+__device__ __forceinline__ void router_dot(const RouterRegs& W, int s0, int cnt, int H,
                                            const void* const (&arow)[RMAX], uint32_t mask,
                                            float (&acc)[RMAX]) {
   constexpr int EL = 4;
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int c = 0; c < kRouterCh; ++c) {
-    int k = ((s0 + c) * 64 + lane) * EL;
-    const bool valid = whole || k < H;
-    k = min(k, H - EL);
-    const float w0 = valid ? __uint_as_float(W.v[0][c].x) : 0.0f;
-    const float w1 = valid ? __uint_as_float(W.v[0][c].y) : 0.0f;
-    const float w2 = valid ? __uint_as_float(W.v[0][c].z) : 0.0f;
-    const float w3 = valid ? __uint_as_float(W.v[0][c].w) : 0.0f;
+    if (c >= cnt) break;
+    const int k = min(((s0 + c) * 64 + lane) * EL, H - EL);
+    const float w0 = __uint_as_float(W.v[0][c].x), w1 = __uint_as_float(W.v[0][c].y);
+    const float w2 = __uint_as_float(W.v[0][c].z), w3 = __uint_as_float(W.v[0][c].w);
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
       if (RMAX > 1 && !(mask & (1u << r))) continue;
@@ -1073,77 +1102,82 @@ __device__ __forceinline__ void router_dot(const RouterRegs& W, int s0, int H, b
   }
 }
 
-/* Tagged store of one router logit part: value bits in the low word, tag in the high word. */
-__device__ __forceinline__ void store_logit_part(const Params& p, int part, int r, int e, float v,
-                                                 uint32_t tag) {
-  st_coh(p.lgp + ((size_t)part * p.R + r) * p.E + e, ((uint64_t)tag << 32) | __float_as_uint(v));
+/* Tagged store of one router logit: value bits in the low word, tag in the high word. */
+__device__ __forceinline__ void store_logit(const Params& p, int r, int e, float v, uint32_t tag) {
+  st_coh(p.lgp + (size_t)r * p.E + e, ((uint64_t)tag << 32) | __float_as_uint(v));
 }
 
-/* Every (expert, part) task stores its partial dot products as tagged values (tag = the launch
- * epoch + 1 in the fused launch, 0 otherwise); the select waits for the tags, so no grid
- * barrier separates the router from the select. With skip (fault injection) nothing is
- * stored. */
+/* Every expert's logit is stored once per row as a tagged value (tag = the launch epoch + 1 in
+ * the fused launch, 0 otherwise); the select waits for the tags, so no grid barrier separates
+ * the router from the select. The sum over a row has a fixed order (steps in a wave, then
+ * waves in order), so every reader sees the same logits. In the local case every wave of the
+ * workgroup passes one __syncthreads here. With skip (fault injection) nothing is stored. */
 template <int ACT, int RMAX, bool PRE>
 __device__ __forceinline__ void ph_router(const Params& p, Smem& sm, const RouterRegs& pre,
                                           uint32_t tag, bool skip) {
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
   const void* arow[RMAX];
   act_rows_ptrs<ACT, RMAX>(p, sm, arow);
   const uint32_t mask = (1u << p.R) - 1u;
-  constexpr int EL = 4;
-  const int nsteps = (p.H + 64 * EL - 1) / (64 * EL);
-  const bool whole = p.H % (64 * EL * kRouterCh) == 0;
+  const int nsteps = (p.H + 255) / 256;
   const RouterTask t = router_task(p);
-  stamp(p, sm.trace_on != 0, 22);
+  /* the first router wave: wave 1 in the local case, else wave 0 */
+  const int tw = t.local ? 64 : 0;
+  stamp(p, sm.trace_on != 0, 22, tw);
   if (t.local) {
     float acc[RMAX];
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) acc[r] = 0.0f;
     if (t.e < p.E) {
-      const int s0 = t.part * kRouterCh;
       if (PRE) {
-        router_dot<ACT, RMAX>(pre, s0, p.H, whole, arow, mask, acc);
+        router_dot<ACT, RMAX>(pre, t.s0, t.cnt, p.H, arow, mask, acc);
       } else {
-        const uint8_t* vr[1] = {reinterpret_cast<const uint8_t*>(p.w_router + (size_t)t.e * p.H)};
-        const uint8_t* sr[1] = {nullptr};
         RouterRegs W;
-        wregs_load(W, vr, sr, p.H, s0);
-        router_dot<ACT, RMAX>(W, s0, p.H, whole, arow, mask, acc);
+        router_load(p, t.e, t.s0, t.cnt, W);
+        router_dot<ACT, RMAX>(W, t.s0, t.cnt, p.H, arow, mask, acc);
       }
     }
-    stamp(p, sm.trace_on != 0, 23);
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
       if (r >= p.R) break;
       const float v = wave_sum(acc[r]);
-      if (lane == 0 && t.e < p.E && !skip) store_logit_part(p, t.part, r, t.e, v, tag);
+      if (lane == 0 && wave > 0) sm.red[wave][r] = v;
     }
+    __syncthreads();
+    /* thread (j, r) sums the parts of expert slot j, row r in wave order */
+    if (tid < t.per * p.R) {
+      const int j = tid / p.R, r = tid % p.R, e = (int)blockIdx.x + j * (int)gridDim.x;
+      if (e < p.E) {
+        float v = 0.0f;
+        for (int w = 1 + j * t.nw; w < 1 + (j + 1) * t.nw; ++w) v += sm.red[w][r];
+        if (!skip) store_logit(p, r, e, v, tag);
+      }
+    }
+    stamp(p, sm.trace_on != 0, 23, 0);
     return;
   }
   const int nwt = gridDim.x * kWaves;
   for (int e = wave_major_id(); e < p.E; e += nwt) {
-    const uint8_t* vr[1] = {reinterpret_cast<const uint8_t*>(p.w_router + (size_t)e * p.H)};
-    const uint8_t* sr[1] = {nullptr};
-    for (int q = 0; q < t.P; ++q) {
-      float part[RMAX];
+    float acc[RMAX];
 #pragma unroll
-      for (int r = 0; r < RMAX; ++r) part[r] = 0.0f;
-      if (PRE && q == 0 && e == wave_major_id()) {
-        router_dot<ACT, RMAX>(pre, 0, p.H, whole, arow, mask, part);
+    for (int r = 0; r < RMAX; ++r) acc[r] = 0.0f;
+    for (int s0 = 0; s0 < nsteps; s0 += kRouterCh) {
+      const int cnt = min(kRouterCh, nsteps - s0);
+      if (PRE && s0 == 0 && e == wave_major_id()) {
+        router_dot<ACT, RMAX>(pre, 0, cnt, p.H, arow, mask, acc);
       } else {
         RouterRegs W;
-        wregs_load(W, vr, sr, p.H, q * kRouterCh);
-        router_dot<ACT, RMAX>(W, q * kRouterCh, p.H, whole, arow, mask, part);
-      }
-#pragma unroll
-      for (int r = 0; r < RMAX; ++r) {
-        if (r >= p.R) break;
-        const float v = wave_sum(part[r]);
-        if (lane == 0 && !skip) store_logit_part(p, q, r, e, v, tag);
+        router_load(p, e, s0, cnt, W);
+        router_dot<ACT, RMAX>(W, s0, cnt, p.H, arow, mask, acc);
       }
     }
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      if (r >= p.R) break;
+      const float v = wave_sum(acc[r]);
+      if (lane == 0 && !skip) store_logit(p, r, e, v, tag);
+    }
   }
-  (void)nsteps;
 }
 
 /* ------------------------------------------------------------------------------------------
@@ -1201,65 +1235,48 @@ __device__ __forceinline__ void key_cx(uint32_t& ah, uint32_t& al, float& as, ui
  * expert index ascending [ds4 page, tie-order commit]. Each lane sorts its PER candidates once;
  * a round takes the largest head over the wave (high word, then low word among the lanes that
  * hold it) and the owning lane pops its head. */
-/* Logits of row r for this lane's experts e = lane + 64 c: the sum of the router's parts in
- * part order. With check, waits (bounded) until every part carries `tag`; returns false on
- * expiry (uniform over the wave). */
+/* Logits of row r for this lane's experts e = lane + 64 c. With check, waits (bounded) until
+ * every one carries `tag`; returns false on expiry (uniform over the wave). */
 template <int PER>
 __device__ __forceinline__ bool gather_logits(const Params& p, const Smem& sm, int r, bool check,
                                               uint32_t tag, float (&z)[PER]) {
   const int lane = threadIdx.x & 63, E = p.E;
-  const int P = (int)router_parts(p.H);
-  const __amdgpu_buffer_rsrc_t lg = coh_region(p.lgp, (size_t)P * p.R * E * 8);
+  const __amdgpu_buffer_rsrc_t lg = coh_region(p.lgp + (size_t)r * E, (size_t)E * 8);
+  uint2 v[PER];
+  bool need[PER];
+  /* every load is issued (a valid repeated address when not needed), so all are in flight
+   * together */
 #pragma unroll
-  for (int c = 0; c < PER; ++c) z[c] = 0.0f;
+  for (int c = 0; c < PER; ++c) {
+    const int e = lane + 64 * c;
+    need[c] = e < E;
+    v[c] = coh_b64(lg, (uint32_t)(e < E ? e : E - 1) * 8u);
+    if (!need[c]) v[c] = make_uint2(0u, tag);
+  }
   bool ok = true;
-  for (int q0 = 0; q0 < P; q0 += 2) {
-    uint2 v[PER][2];
-    bool need[PER][2];
+  if (check) {
+    auto pending = [&]() {
+      bool any = false;
 #pragma unroll
-    for (int c = 0; c < PER; ++c)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int e = lane + 64 * c, q = q0 + h;
-        need[c][h] = e < E && q < P;
-        /* every load is issued (a valid repeated address when not needed), so all are in
-         * flight together */
-        const int ee = e < E ? e : E - 1, qq = q < P ? q : P - 1;
-        v[c][h] = coh_b64(lg, (uint32_t)((((size_t)qq * p.R + r) * E + ee) * 8));
-        if (!need[c][h]) v[c][h] = make_uint2(0u, tag);
-      }
-    if (check) {
-      auto pending = [&]() {
-        bool any = false;
+      for (int c = 0; c < PER; ++c) any |= need[c] && v[c].y != tag;
+      return any;
+    };
+    if (__ballot(pending()) != 0ull) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__ballot(pending()) != 0ull) {
+        __builtin_amdgcn_s_sleep(1);
 #pragma unroll
         for (int c = 0; c < PER; ++c)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) any |= need[c][h] && v[c][h].y != tag;
-        return any;
-      };
-      if (__ballot(pending()) != 0ull) {
-        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        while (__ballot(pending()) != 0ull) {
-          __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-          for (int c = 0; c < PER; ++c)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-              if (need[c][h] && v[c][h].y != tag)
-                v[c][h] = coh_b64(lg, (uint32_t)((((size_t)(q0 + h) * p.R + r) * E + lane + 64 * c) * 8));
-          if (__builtin_amdgcn_s_memrealtime() - t0 > sm.spin) {
-            ok = false;
-            break;
-          }
+          if (need[c] && v[c].y != tag) v[c] = coh_b64(lg, (uint32_t)(lane + 64 * c) * 8u);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > sm.spin) {
+          ok = false;
+          break;
         }
       }
     }
-#pragma unroll
-    for (int c = 0; c < PER; ++c)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        if (need[c][h]) z[c] += __uint_as_float(v[c][h].x);
   }
+#pragma unroll
+  for (int c = 0; c < PER; ++c) z[c] = need[c] ? __uint_as_float(v[c].x) : 0.0f;
   return ok;
 }
 
@@ -3077,7 +3094,7 @@ __global__ void __launch_bounds__(kBlock) k_expand(Params p) {
 /* The whole layer half in one persistent launch (one workgroup per compute unit), with no grid
  * barrier: every value one workgroup hands to another carries this launch's tag and the reader
  * polls for it (bounded).
- *   mix partials (tagged) | pre side in every workgroup (gathers the partials) | router parts
+ *   mix partials (tagged) | pre side in every workgroup (gathers the partials) | router logits
  *   (tagged) beside Sinkhorn | select of every row (gathers the parts) while free waves claim
  *   the shared expert's gate/up rows | plan | routed gate/up strided over the grid (tagged
  *   hidden rows) | down in groups staged as their hidden rows arrive, block | expand + carry
@@ -3085,8 +3102,9 @@ __global__ void __launch_bounds__(kBlock) k_expand(Params p) {
  * Trace slots: 0 start, 1 mix partials, 2 pre-side inputs ready, 3 pre side, 4 router,
  * 5 shared gate/up, 6 select rows, 7 select finished, 8 plan, 9 routed gate/up,
  * 10 routed down (several rows), 11 down + block, 12 expand, 13 carry; 14-18 inside the pre
- * side, 19 select scores, 20 shared down (several rows), 21 first down group staged, 22-24
- * router start, router dots, logits gathered, 25-31 gate/up end of waves 1-7. */
+ * side, 19 select scores, 20 shared down (several rows), 21 first down group staged, 22 router
+ * start (first router wave), 23 router logits stored, 24 logits gathered, 25-31 gate/up end of
+ * waves 1-7. */
 template <int ACT, int RFMT, int SFMT, int RMAX>
 __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   __shared__ Smem sm;
@@ -3117,14 +3135,15 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   }
   __syncthreads();
   stamp(p, tr, 2);
+  if (!p.carry_in) warm_state<ACT>(p, sm);
   if (!ph_hc_pre<ACT, RMAX>(p, sm, blockIdx.x == 0, true, tag)) return;
   if (p.state_out == p.state) { /* in place: tell the expands this workgroup is done reading */
     __syncthreads();
     if (threadIdx.x == 0) st_coh(p.pre_done + blockIdx.x, (uint64_t)tag);
   }
   stamp(p, tr, 3);
-  /* router parts (waves 1 ..), then the select (waves 0 .. R - 1, polling the tagged logits),
-   * then the shared expert's gate/up rows, claimed by whichever waves are free */
+  /* router logits (waves 1 ..), then the select (waves 0 .. R - 1, polling the tagged logits)
+   * beside the shared expert's gate/up rows, claimed by whichever waves are free */
   ph_router<ACT, RMAX, true>(p, sm, rpre, tag, sm.skip_phase == PH_ROUTER);
   stamp(p, tr, 4);
   ph_sinkhorn(p, sm, blockIdx.x == 0); /* comb is needed only by the expand */
