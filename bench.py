@@ -371,6 +371,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-rows6", action="store_true", help="skip the 6- and 8-row workloads")
     ap.add_argument("--no-chain", action="store_true", help="skip the 8-layer chain")
+    ap.add_argument("--no-drafts", action="store_true",
+                    help="skip the draft routing shapes (128 experts top-3, 256 experts top-6)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run a plain device copy of this size (counter calibration)")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
@@ -436,6 +438,20 @@ def main():
                               bytes_per_step=rx["bytes_per_step_mean"])
             del wx
             torch.cuda.empty_cache()
+    if not args.no_drafts:
+        drafts = {}
+        for ci in synth.DRAFT_CONFIGS:
+            cfgx = synth.CONFIGS[ci]
+            wx = Workload(cfgx, args.copies)
+            rx = summarize(wx.run(args.steps, args.warmup), cfgx)
+            log("  draft %d:" % ci, json.dumps(rx))
+            drafts["e%d_k%d_r%d" % (cfgx.n_experts, cfgx.top_k, cfgx.rows)] = dict(
+                workload=cfgx.name, steps_per_s=rx["steps_per_s"],
+                launch_us_median=rx["launch_us_median"], achieved_gbs=rx["achieved_gbs"],
+                frac=rx["achieved_gbs"] / PEAK_HBM_GBS, bytes_per_step=rx["bytes_per_step_mean"])
+            del wx
+            torch.cuda.empty_cache()
+        extra["drafts"] = drafts
     if not args.no_chain:
         cfg5 = synth.CONFIGS[5]
         wc = ChainWorkload(cfg5)

@@ -211,7 +211,18 @@ CONFIGS: Dict[int, Config] = {
               2048, 2048, FMT_BF16, FMT_MXFP4, FMT_BF16, 2.5, grouped_bias=True, zero_rows=(7,)),
     5: Config(5, "chain of 8 V4.1-like bf16 layer halves, 1 row", 1, 5120, 256, 8, 2048, 2048,
               FMT_BF16, FMT_BF16, FMT_BF16, 2.5, layers=8),
+    # draft-stage routing shapes: 128 experts with top-3 (the draft stages) and 256 experts
+    # with top-6 (the single-box ds4 router), at the same hidden and expert widths
+    6: Config(6, "draft MoE half, 128 experts top-3, 1 row, bf16 experts", 1, 5120, 128, 3, 2048,
+              2048, FMT_BF16, FMT_BF16, FMT_BF16, 2.5),
+    7: Config(7, "draft MoE half, 128 experts top-3, 6 rows, Q8_0 experts", 6, 5120, 128, 3, 2048,
+              2048, FMT_BF16, FMT_Q8_0, FMT_Q8_0, 2.5),
+    8: Config(8, "MoE half, 256 experts top-6, 1 row, bf16 experts", 1, 5120, 256, 6, 2048, 2048,
+              FMT_BF16, FMT_BF16, FMT_BF16, 2.5),
+    9: Config(9, "MoE half, 256 experts top-6, 6 rows, Q8_0 experts", 6, 5120, 256, 6, 2048, 2048,
+              FMT_BF16, FMT_Q8_0, FMT_Q8_0, 2.5),
 }
+DRAFT_CONFIGS = (6, 7, 8, 9)
 
 
 def _act_normal(act: str) -> int:

@@ -438,11 +438,13 @@ def compare_end_to_end(cfg: synth.Config, out: Dict[str, np.ndarray], state_h, d
     {"skipped": rows} and nothing is compared (the stage-wise comparison covers those rows).
     The oracle's outputs are returned under "ref" either way.
 
-    Error budget. Up to the hidden rows every tensor is held to the contract and step rules.
-    From there on a legitimate rounding flip of a hidden value (one bf16 step) reaches every
-    output of the down projection, and cancellation between routed and shared can enlarge it
-    again, so each later tensor may differ by its own contract tolerance plus the first-order
-    effect of the measured differences of its inputs through the absolute values of the weights:
+    Error budget. The bf16 tensors (x, norm, hidden rows) are held to the contract and step
+    rules. A legitimate rounding flip (one bf16 step) of a norm value reaches every logit, and
+    one of a hidden value every output of the down projection, and cancellation between routed
+    and shared can enlarge it again, so each later tensor may differ by its own contract
+    tolerance plus the first-order effect of the measured differences of its inputs through the
+    absolute values of the weights:
+      logits:  |W_r| . |dnorm|        weights: d(rho s_j / sum s) through ds = s'(z) dz
       routed:  sum_j |w_j| (|W_d[e_j]| . |dh_j|)              shared: |W_ds| . |dh_s|
       block:   the allowed differences of routed and shared
       new:     post * (the allowed difference of block)
@@ -457,12 +459,30 @@ def compare_end_to_end(cfg: synth.Config, out: Dict[str, np.ndarray], state_h, d
         return {"skipped": near, "ref": ref}
     rep = {"ref": ref}
     R, H, K = cfg.rows, cfg.hidden, cfg.top_k
-    for key in ("mixes", "pre", "post", "logits", "weights"):
+    for key in ("mixes", "pre", "post"):
         rep[key] = check_f32("e2e " + key, out[key], ref[key])
     rep["comb"] = check_f32("e2e comb", out["comb"].reshape(R, 16), ref["comb"].reshape(R, 16))
     assert np.array_equal(out["idx"], ref["idx"]), (out["idx"], ref["idx"])
     for key in ("x", "norm"):
         rep[key] = check_bf16("e2e " + key, out[key], ref[key], act)
+    f64 = lambda a: as_f32(a, act).astype(np.float64)
+    # a legitimate one-step flip of a norm value reaches every logit through |W_r|, and the
+    # weights through the derivative of s = sqrt(softplus(z)) and the row division
+    dnorm = np.abs(f64(out["norm"]) - f64(ref["norm"]))                    # [R][H]
+    ext_lg = dnorm @ np.abs(np.asarray(dense_h["w_router"], np.float64)).T  # [R][E]
+    rep["logits"] = check_f32("e2e logits", out["logits"], ref["logits"], extra=ext_lg)
+    z = np.asarray(ref["logits"], np.float64)
+    zr = np.sqrt((z * z).mean(axis=1, keepdims=True))
+    dz = F32_TOL * np.maximum(np.abs(z), zr) + ext_lg
+    sp = np.logaddexp(0.0, z)
+    sc = np.sqrt(sp)
+    ds = dz / (1.0 + np.exp(-z)) / (2.0 * np.maximum(sc, 1e-30))          # |ds/dz| dz
+    idx = np.asarray(ref["idx"])
+    ssel = np.take_along_axis(sc, idx, axis=1)
+    dsel = np.take_along_axis(ds, idx, axis=1)
+    tot = np.maximum(ssel.sum(axis=1, keepdims=True), 2.0 ** -14)
+    ext_w = cfg.routed_scale * (dsel / tot + ssel * dsel.sum(axis=1, keepdims=True) / tot ** 2)
+    rep["weights"] = check_f32("e2e weights", out["weights"], ref["weights"], extra=ext_w)
     cache = {}
     getx = lambda e: cache.setdefault(e, routed_get(e))
     rep["h_routed"] = check_hidden("e2e h_routed", out["h_routed"], ref["h_routed"], act,
@@ -471,7 +491,6 @@ def compare_end_to_end(cfg: synth.Config, out: Dict[str, np.ndarray], state_h, d
     if cfg.shared_inter > 0:
         rep["h_shared"] = check_hidden("e2e h_shared", out["h_shared"], ref["h_shared"], act,
                                        out["norm"], lambda r_: (cfg.shared_fmt, shared_h, r_[0]))
-    f64 = lambda a: as_f32(a, act).astype(np.float64)
     dh = np.abs(f64(out["h_routed"]) - f64(ref["h_routed"]))            # [R][K][I]
     w = np.abs(np.asarray(ref["weights"], np.float64))
     ext_routed = np.zeros((R, H))

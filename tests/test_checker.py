@@ -93,3 +93,31 @@ def test_hidden_value_from_an_ambiguous_rounding_is_accepted():
     bad = support._bf16_bits(support.bf(ref).astype(np.float64) * 1.03)
     with pytest.raises(AssertionError, match="exact g"):
         support.check_hidden("h", bad, ref, "bf16", norm, rows)
+
+
+def test_norm_flip_reaches_logits_within_budget_only():
+    """A one-step flip of a norm value moves every logit by W_r[e][h] times the step; the end to
+    end check allows exactly that first-order effect, and a logit error it does not explain
+    still fails."""
+    out, args = oracle_as_gpu(CFG)
+    s = oracle.shape_of(CFG)
+    d0 = args[1]
+    norm = out["norm"].copy()
+    h = int(np.argmax(np.abs(support.bf(norm[0]))))
+    norm[0, h] ^= 1
+    flipped = dict(out)
+    flipped["norm"] = norm
+    flipped["logits"] = oracle.router_logits(s, norm, d0["w_router"])
+    moved = np.abs(flipped["logits"][0].astype(np.float64) - out["logits"][0])
+    lim = support.F32_TOL * np.maximum(np.abs(out["logits"][0]),
+                                       np.sqrt((out["logits"][0].astype(np.float64) ** 2).mean()))
+    assert (moved > lim).any(), "the flip must move some logit beyond the plain tolerance"
+    rep = support.compare_end_to_end(CFG, flipped, *args)
+    assert "skipped" not in rep
+    bad = dict(flipped)
+    lg = flipped["logits"].copy()
+    e = int(np.argmax(np.abs(lg[1])))
+    lg[1, e] *= np.float32(1.001)   # row 1 has no flipped norm value
+    bad["logits"] = lg
+    with pytest.raises(AssertionError, match="e2e logits"):
+        support.compare_end_to_end(CFG, bad, *args)

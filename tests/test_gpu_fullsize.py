@@ -6,7 +6,9 @@ Workloads: hidden 5120, 256 experts, top-8, inter 2048, shared inter 2048, rho 2
   * 1 row and bf16 experts,
   * 6 rows and Q8_0 experts,
   * 8 rows, MXFP4 routed + bf16 shared experts, row 7 all zero, bias grouped by 32,
-  * a chain of 8 bf16 layer halves at 1 row linked by the next-pre carry.
+  * a chain of 8 bf16 layer halves at 1 row linked by the next-pre carry;
+and the draft routing shapes at the same widths: 128 experts with top-3 and 256 experts with
+top-6, each at 1 row (bf16 experts) and 6 rows (Q8_0 experts).
 """
 
 import numpy as np
@@ -25,7 +27,7 @@ def _host(cfg, layer):
     return synth.dense_host(cfg, layer), shared
 
 
-@pytest.mark.parametrize("ci", [2, 3, 4])
+@pytest.mark.parametrize("ci", [2, 3, 4, *synth.DRAFT_CONFIGS])
 def test_full_size_layer(ci):
     import torch
     import support

@@ -38,6 +38,11 @@ CASES = {
     # one-row down flow, so the fused launch takes the grouped per-slice down phase
     "bf16_r1_k16_wide": C2.with_(hidden=512, n_experts=64, top_k=16, inter=2560,
                                  shared_inter=2560),
+    # draft routing shapes: 128 experts top-3 (half the workgroups have no router row) and
+    # 256 experts top-6
+    "draft_e128_k3_r1": synth.CONFIGS[6].with_(hidden=512, inter=256, shared_inter=256),
+    "draft_e128_k3_r6_q8": synth.CONFIGS[7].with_(hidden=512, inter=256, shared_inter=256),
+    "e256_k6_r6_q8": synth.CONFIGS[9].with_(hidden=512, inter=256, shared_inter=256),
 }
 
 OUT_KEYS = ["mixes", "pre", "post", "comb", "x", "norm", "logits", "idx", "weights",

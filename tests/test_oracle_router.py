@@ -46,11 +46,18 @@ def _scores(logits, bias):
     return s, beta
 
 
-@pytest.mark.parametrize("seed", range(30))
-def test_select_matches_brute_force_sort(seed):
+# 30 random small shapes, then the draft routing shapes (128 experts top-3, 256 top-6)
+SELECT_CASES = [(seed, None, None) for seed in range(30)] + [
+    (100 + i, E, k) for i, (E, k) in enumerate([(128, 3), (128, 3), (128, 3), (256, 6),
+                                                (256, 6), (256, 6)])]
+
+
+@pytest.mark.parametrize("seed,E,k", SELECT_CASES)
+def test_select_matches_brute_force_sort(seed, E, k):
     rng = np.random.default_rng(seed)
-    E = int(rng.integers(2, 17))
-    k = int(rng.integers(1, E + 1))
+    if E is None:
+        E = int(rng.integers(2, 17))
+        k = int(rng.integers(1, E + 1))
     rho = float(rng.choice([1.0, 2.5]))
     s = shape(E, k, rho)
     mode = seed % 3
@@ -124,7 +131,7 @@ def test_zero_row_grouped_bias_closed_form():
     np.testing.assert_allclose(w[0], cfg.routed_scale / 8, rtol=2e-7)
 
 
-@pytest.mark.parametrize("ci", [2, 3, 4])
+@pytest.mark.parametrize("ci", [2, 3, 4, 6, 7, 8, 9])
 def test_weights_sum_to_scale_on_workload_rows(ci):
     cfg = synth.CONFIGS[ci]
     s = oracle.shape_of(cfg)
