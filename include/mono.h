@@ -147,11 +147,21 @@ mono_status mono_workspace_set_debug(void* ws, uint32_t spin_limit_ticks, int32_
  * rows, 7 select finished, 8 plan, 9 routed gate/up, 10 routed down (several rows), 11 down +
  * block, 12 expand, 13 carry;
  * 14-18 inside the pre side (raw sums, mixes, gates, collapse, sum of squares), 19 select
- * scores, 20 shared down (several rows), 21 first down group staged, 22 router start,
- * 23 router dots, 24 logits gathered,
+ * scores, 20 shared down (several rows), 21 first down group staged, 22 router start (first
+ * router wave), 23 router logits stored, 24 logits gathered,
  * 25-31 routed gate/up done in waves 1-7 (slot 9 is wave 0).
  * Enqueued on `stream`. */
 mono_status mono_workspace_set_trace(void* ws, int enable, void* stream);
+
+/* Debug mode (race shaker): when max_ticks != 0, mono_ffn_layer launches on this workspace
+ * issued after the call make every wave wait, at each phase boundary, a pseudo-random time in
+ * [0, max_ticks) ticks of the 100 MHz real-time counter, drawn from (seed, launch epoch,
+ * workgroup, wave, boundary). The results do not depend on timing, so they must stay
+ * byte-identical to a launch without delays; a difference or an expired wait points at a race. max_ticks above MONO_JITTER_MAX_TICKS (a delay of 0.1 ms) is
+ * refused with MONO_E_INVAL; 0 turns it off, as does mono_workspace_init. A host-side setting
+ * (kept per workspace address, thread-safe); nothing is enqueued. Not for the hot path. */
+#define MONO_JITTER_MAX_TICKS 10000u
+mono_status mono_workspace_set_jitter(void* ws, uint32_t max_ticks, uint32_t seed);
 
 /* Intermediate tensors kept in the workspace by mono_ffn_layer (and by the unfused calls, for
  * the tensors they produce internally), for inspection after the stream has synchronised. */

@@ -23,10 +23,12 @@ MONO_OK, MONO_E_INVAL, MONO_E_UNSUPPORTED, MONO_E_DEVICE, MONO_E_TIMEOUT = 0, -1
  MONO_T_BLOCK, MONO_T_CARRY, MONO_T_TRACE) = range(16)
 
 EXPORTS = ("mono_workspace_bytes", "mono_workspace_init", "mono_workspace_poll",
-           "mono_workspace_set_debug", "mono_workspace_set_trace", "mono_workspace_tensor", "mono_last_error",
+           "mono_workspace_set_debug", "mono_workspace_set_trace", "mono_workspace_set_jitter",
+           "mono_workspace_tensor", "mono_last_error",
            "mono_grid_size", "mono_hc_mix_collapse", "mono_router_select", "mono_moe_experts",
            "mono_hc_expand", "mono_ffn_layer", "mono_ffn_layer_static")
 MONO_STATIC_WS_BYTES = 8 << 20
+MONO_JITTER_MAX_TICKS = 10000
 
 
 class MonoError(RuntimeError):
@@ -76,6 +78,7 @@ def lib() -> ctypes.CDLL:
             "mono_workspace_poll": (I, [P, ctypes.POINTER(ctypes.c_uint32), P]),
             "mono_workspace_set_debug": (I, [P, ctypes.c_uint32, ctypes.c_int32, ctypes.c_int32, P]),
             "mono_workspace_set_trace": (I, [P, I, P]),
+            "mono_workspace_set_jitter": (I, [P, ctypes.c_uint32, ctypes.c_uint32]),
             "mono_workspace_tensor": (I, [SP, P, I, ctypes.POINTER(ctypes.c_void_p),
                                           ctypes.POINTER(ctypes.c_size_t)]),
             "mono_last_error": (ctypes.c_char_p, []),
@@ -154,6 +157,10 @@ def mono_workspace_set_debug(ws, spin_limit_ticks=0, fault_wg=-1, fault_phase=0,
 
 def mono_workspace_set_trace(ws, enable=True, stream=None) -> None:
     _ok(lib().mono_workspace_set_trace(ptr(ws), 1 if enable else 0, stream))
+
+
+def mono_workspace_set_jitter(ws, max_ticks=0, seed=0) -> None:
+    _ok(lib().mono_workspace_set_jitter(ptr(ws), max_ticks, seed))
 
 
 def mono_workspace_poll(ws, stream=None):

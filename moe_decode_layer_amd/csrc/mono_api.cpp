@@ -14,6 +14,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <utility>
+#include <unordered_map>
+#include <mutex>
+#include <atomic>
 
 #include "mono_internal.h"
 
@@ -260,6 +264,31 @@ size_t mono_workspace_bytes(const mono_shape* shape) {
   return ws_layout(*shape).total;
 }
 
+/* Race-shaker settings per workspace (host side; read by every fused launch on it). */
+static std::mutex g_jitter_mu;
+static std::unordered_map<const void*, std::pair<uint32_t, uint32_t>> g_jitter;
+static std::atomic<int> g_jitter_n{0};
+
+static void jitter_of(const void* ws, uint32_t& max_ticks, uint32_t& seed) {
+  max_ticks = seed = 0;
+  if (g_jitter_n.load(std::memory_order_relaxed) == 0) return;
+  std::lock_guard<std::mutex> lk(g_jitter_mu);
+  const auto it = g_jitter.find(ws);
+  if (it != g_jitter.end()) {
+    max_ticks = it->second.first;
+    seed = it->second.second;
+  }
+}
+
+static void jitter_set(const void* ws, uint32_t max_ticks, uint32_t seed) {
+  std::lock_guard<std::mutex> lk(g_jitter_mu);
+  if (max_ticks)
+    g_jitter[ws] = std::make_pair(max_ticks, seed);
+  else
+    g_jitter.erase(ws);
+  g_jitter_n.store((int)g_jitter.size(), std::memory_order_relaxed);
+}
+
 mono_status mono_workspace_init(void* ws, const mono_shape* shape, void* stream) {
   Check c;
   check_shape(c, shape);
@@ -270,6 +299,7 @@ mono_status mono_workspace_init(void* ws, const mono_shape* shape, void* stream)
     const WsLayout W = ws_layout(*shape);
     p.tag_words = (W.lgp_end - W.carry_part) / 8;
   }
+  jitter_set(ws, 0, 0);
   const int rc = launch(K_WS_INIT, p, shape->act, 0, 0, 1, stream);
   if (rc != 0) {
     g_error = std::string("workspace init: ") + hipGetErrorString((hipError_t)rc);
@@ -303,6 +333,18 @@ mono_status mono_workspace_set_trace(void* ws, int enable, void* stream) {
     g_error = std::string("set_trace: ") + hipGetErrorString((hipError_t)rc);
     return MONO_E_DEVICE;
   }
+  g_error.clear();
+  return MONO_OK;
+}
+
+mono_status mono_workspace_set_jitter(void* ws, uint32_t max_ticks, uint32_t seed) {
+  Check c;
+  c.ptr(ws, "ws", 256);
+  if (max_ticks > MONO_JITTER_MAX_TICKS)
+    c.fail(MONO_E_INVAL, "set_jitter: max_ticks %u exceeds MONO_JITTER_MAX_TICKS (%u)", max_ticks,
+           (unsigned)MONO_JITTER_MAX_TICKS);
+  if (c.code != MONO_OK) return c.done();
+  jitter_set(ws, max_ticks, seed);
   g_error.clear();
   return MONO_OK;
 }
@@ -511,6 +553,7 @@ mono_status mono_ffn_layer(const mono_shape* shape, const mono_layer* layer,
   if (c.code == MONO_OK) check_resident(c, shape, rf, sf);
   if (c.code != MONO_OK) return c.done();
   Params p = base_params(shape, layer, ws, grid);
+  jitter_of(ws, p.jitter, p.jseed);
   const WsLayout W = ws_layout(*shape);
   uint8_t* b = static_cast<uint8_t*>(ws);
   p.state = state_in; p.carry_in = carry_in; p.w_mix_next = w_mix_next;

@@ -550,6 +550,29 @@ __device__ __forceinline__ void stamp(const Params& p, bool on, int slot, int th
     p.trace[(size_t)blockIdx.x * kTraceSlots + slot] = __builtin_amdgcn_s_memrealtime();
 }
 
+/* Race shaker (debug mode; off unless mono_workspace_set_jitter set a nonzero limit for the
+ * workspace): this wave waits a pseudo-random number of real-time ticks below p.jitter (at most
+ * MONO_JITTER_MAX_TICKS), drawn from the seed, the launch epoch, the workgroup, the wave and
+ * `salt` through the lowbias32 integer hash (C. Wellons). The delays at the phase boundaries
+ * reorder both the workgroups' publications and the waves' task claims inside a workgroup. The
+ * results of a launch do not depend on the timing of its waves, so any difference under the
+ * shaker is a race. Off, it costs a test of a kernel argument per boundary (none inside the
+ * task loops). */
+__device__ __forceinline__ void shake(const Params& p, const Smem& sm, uint32_t salt) {
+  if (p.jitter == 0u) return;
+  const uint32_t J = p.jitter < MONO_JITTER_MAX_TICKS ? p.jitter : MONO_JITTER_MAX_TICKS;
+  uint32_t h = p.jseed + 0x9E3779B9u * (uint32_t)(sm.epoch + 1) + 0x85EBCA6Bu * blockIdx.x +
+               0xC2B2AE35u * (threadIdx.x >> 6) + 0x27D4EB2Fu * salt;
+  h ^= h >> 16;
+  h *= 0x7FEB352Du;
+  h ^= h >> 15;
+  h *= 0x846CA68Bu;
+  h ^= h >> 16;
+  h = __builtin_amdgcn_readfirstlane(h);
+  const uint64_t d = h % J, t0 = __builtin_amdgcn_s_memrealtime();
+  while (__builtin_amdgcn_s_memrealtime() - t0 < d) __builtin_amdgcn_s_sleep(4);
+}
+
 /* Task order for phases with fewer tasks than waves: consecutive tasks go to different compute
  * units first (task t -> workgroup t % G, wave t / G). */
 __device__ __forceinline__ int wave_major_id() {
@@ -2451,6 +2474,7 @@ __device__ __forceinline__ bool ph_down(const Params& p, Smem& sm, uint32_t htag
     if (FUSED && k0 == 0) {
       slice_store(p, c, sm, sreg);
       stamp(p, sm.trace_on != 0, 21);
+      shake(p, sm, 21);
     }
     for (int t = wave; t < ntask; t += kWaves) {
       const int it = down_item(p, sm, k0 + t / nq), q = t % nq;
@@ -2809,6 +2833,7 @@ __device__ __forceinline__ bool ph_down_em(const Params& p, Smem& sm, uint32_t h
     if (first) {
       slice_store(p, c, sm, sreg);
       stamp(p, sm.trace_on != 0, 21);
+      shake(p, sm, 21);
       first = false;
     }
     if (with_sh) {
@@ -2818,6 +2843,7 @@ __device__ __forceinline__ bool ph_down_em(const Params& p, Smem& sm, uint32_t h
                                       Kp, tag);
       }
       stamp(p, sm.trace_on != 0, 20);
+      shake(p, sm, 20);
     }
     const int qa = q0 > u * nqi ? q0 : u * nqi, qb = q1 < u1 * nqi ? q1 : u1 * nqi;
     if (qa < qb) em_routed_blocks<ACT, RFMT, RMAX>(p, sm, qa, qb, nqi, Kp, tag);
@@ -2825,6 +2851,7 @@ __device__ __forceinline__ bool ph_down_em(const Params& p, Smem& sm, uint32_t h
   }
   if (first) slice_store(p, c, sm, sreg);
   stamp(p, sm.trace_on != 0, 10);
+  shake(p, sm, 10);
   const DownGeo g = down_geo(p, sm);
   if (!em_gather_y(p, sm, g.h0, g.nh, Kp, g.y, tag)) return false;
   for (int q = tid; q < g.nh * R; q += kBlock) {
@@ -2958,6 +2985,7 @@ __device__ __forceinline__ void ph_expand(const Params& p, Smem& sm, const float
   }
   if (p.w_mix_next == nullptr) return;
   stamp(p, sm.trace_on != 0, 12);
+  shake(p, sm, 12);
   __syncthreads();
   /* carry partials of this slice: cp[j][r][hl] = sum_i W_next[j][i H + h] new[r][i] (j < 24),
    * cp[24][r][hl] = sum_i new[r][i]^2; then summed over hl in order */
@@ -3112,6 +3140,7 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   __syncthreads();
   const bool tr = sm.trace_on != 0;
   stamp(p, tr, 0);
+  shake(p, sm, 0);
   /* values exchanged between workgroups carry this launch's tag: no grid barrier */
   const uint32_t tag = (uint32_t)(sm.epoch + 1);
   RouterRegs rpre;
@@ -3122,6 +3151,7 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
     t0 = busy < kWaves ? busy * 64 : 0;
     ph_mix_partials<ACT, RMAX>(p, tag, sm.skip_phase == PH_MIX);
     stamp(p, tr, 1);
+    shake(p, sm, 1);
   }
   router_prefetch(p, rpre);
   load_pre_params<ACT>(p, sm, t0);
@@ -3135,6 +3165,7 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   }
   __syncthreads();
   stamp(p, tr, 2);
+  shake(p, sm, 2);
   if (!p.carry_in) warm_state<ACT>(p, sm);
   if (!ph_hc_pre<ACT, RMAX>(p, sm, blockIdx.x == 0, true, tag)) return;
   if (p.state_out == p.state) { /* in place: tell the expands this workgroup is done reading */
@@ -3142,10 +3173,12 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
     if (threadIdx.x == 0) st_coh(p.pre_done + blockIdx.x, (uint64_t)tag);
   }
   stamp(p, tr, 3);
+  shake(p, sm, 3);
   /* router logits (waves 1 ..), then the select (waves 0 .. R - 1, polling the tagged logits)
    * beside the shared expert's gate/up rows, claimed by whichever waves are free */
   ph_router<ACT, RMAX, true>(p, sm, rpre, tag, sm.skip_phase == PH_ROUTER);
   stamp(p, tr, 4);
+  shake(p, sm, 4);
   ph_sinkhorn(p, sm, blockIdx.x == 0); /* comb is needed only by the expand */
   /* hidden rows carry a 16-bit tag of this launch (never 0, the value the init leaves) */
   const uint32_t htag = (uint32_t)(sm.epoch % 65535u) + 1u;
@@ -3166,10 +3199,13 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   __syncthreads();
   if (!select_finish(p, sm, blockIdx.x == 0)) return;
   stamp(p, tr, 7);
+  shake(p, sm, 7);
   ph_plan(p, sm);
   stamp(p, tr, 8);
+  shake(p, sm, 8);
   ph_gateup_routed<ACT, RFMT, RMAX>(p, sm, htag, hskip);
   stamp(p, tr, 9);
+  shake(p, sm, 9);
   /* end of each other wave's gate/up rows: slots 25 .. 31 */
   if (tr && (threadIdx.x & 63) == 0 && threadIdx.x > 0)
     p.trace[(size_t)blockIdx.x * kTraceSlots + 24 + (threadIdx.x >> 6)] =
@@ -3193,6 +3229,7 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
     }
   }
   stamp(p, tr, 11);
+  shake(p, sm, 11);
   const DownGeo g = down_geo(p, sm);
   ph_expand<ACT, RMAX, true>(p, sm, g.blk);
   stamp(p, tr, 13);

@@ -78,6 +78,7 @@ __global__ void k_ws_trace(uint32_t* ctl, uint32_t on) {
   if (threadIdx.x == 0) ctl[CTL_TRACE] = on;
 }
 
+
 int launch(Kernel k, const Params& p, int act, int rfmt, int sfmt, int grid, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (k == K_WS_INIT) {

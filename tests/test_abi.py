@@ -163,3 +163,13 @@ def test_static_workspace_refuses_shapes_beyond_its_size():
         B.mono_ffn_layer_static(s, layer(), None, P16, None, P16, None)
     assert e.value.status == B.MONO_E_UNSUPPORTED
     assert "static workspace" in e.value.message
+
+
+def test_race_shaker_limit_is_checked_before_any_device_work():
+    with pytest.raises(B.MonoError) as e:
+        B.mono_workspace_set_jitter(P256, B.MONO_JITTER_MAX_TICKS + 1, 7)
+    assert e.value.status == B.MONO_E_INVAL
+    assert "MONO_JITTER_MAX_TICKS" in e.value.message
+    with pytest.raises(B.MonoError) as e:
+        B.mono_workspace_set_jitter(P256 + 16, 100, 7)
+    assert "ws is not 256-byte aligned" in e.value.message

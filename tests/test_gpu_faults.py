@@ -1,5 +1,5 @@
 """Failure handling of the persistent launch, forced from the host: workgroup 0 withholds the
-values it publishes for the other workgroups (its mix partial sums, router logit parts or hidden
+values it publishes for the other workgroups (its mix partial sums, router logits or hidden
 rows) and the wait limit is shortened, so every waiting workgroup's bounded wait expires, the
 error word is set and the launch ends normally (no hang, no fault). After mono_workspace_init
 the workspace works again and gives the same bytes as a fresh one."""
