@@ -71,6 +71,7 @@ def lib():
             "or_mix": [SP, P, P, P, P],
             "or_split": [SP, P, P, P, P, P, P],
             "or_collapse_norm": [SP, P, P, P, P, P],
+            "or_head": [SP, P, P, P, P, P, P, P, P],
             "or_router_logits": [SP, P, P, P],
             "or_select": [SP, P, P, P, P, P],
             "or_expert_hidden": [SP, ctypes.c_int, ctypes.POINTER(Expert), P, P],
@@ -158,6 +159,16 @@ def collapse_norm(s: Shape, state, pre, w_norm):
     _check(lib().or_collapse_norm(ctypes.byref(s), _p(state), _p(pre), _p(w_norm), _p(x),
                                   _p(norm)), "collapse_norm")
     return x, norm
+
+
+def head(s: Shape, state, w_head, head_scale, head_base, w_norm):
+    """Model tail: (pre [R][4], x [R][H], norm [R][H]) without a split."""
+    pre = np.zeros((s.rows, 4), np.float32)
+    x = np.zeros((s.rows, s.hidden), _act_dtype(s))
+    norm = np.zeros((s.rows, s.hidden), _act_dtype(s))
+    _check(lib().or_head(ctypes.byref(s), _p(state), _p(w_head), _p(head_scale), _p(head_base),
+                         _p(w_norm), _p(pre), _p(x), _p(norm)), "head")
+    return pre, x, norm
 
 
 def router_logits(s: Shape, norm, w_router) -> np.ndarray:

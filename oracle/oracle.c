@@ -293,6 +293,49 @@ int or_collapse_norm(const or_shape* s, const void* state, const float* pre, con
 }
 
 /* ---------------------------------------------------------------------------------------------
+ * Model tail [ds4 single-box commit: the logits' collapse and the output norm reuse the collapse
+ * kernel without a split; sgl3 Modifications: the last FFN post deferred to the model tail].
+ * READING: the head has its own 4-row mix W_head [4][4H], one scale a and four biases b; its
+ * pre weights are the pre half of the split and there is no post, comb or Sinkhorn:
+ *   m[i]   = f32( (sum_t W_head[i][t] s[t]) / sqrt(mean(s^2) + eps_hc) )   (as the mix)
+ *   pre[i] = f32( sigmoid(a * m[i] + b[i]) )                              (as the split's pre)
+ *   x, norm = the pre-weighted collapse and weighted RMSNorm above, with the output norm weight.
+ * pre [R][4] (optional), x and norm [R][H] (act). */
+int or_head(const or_shape* s, const void* state, const float* w_head, const float* head_scale,
+            const float* head_base, const void* w_norm, float* pre, void* x, void* norm) {
+  if (!shape_ok(s) || !state || !w_head || !head_scale || !head_base || !w_norm || !x || !norm)
+    return -1;
+  const int64_t n = (int64_t)NSTREAM * s->hidden;
+  float* pw = (float*)malloc(sizeof(float) * (size_t)(s->rows > 0 ? s->rows : 1) * NSTREAM);
+  double* v = (double*)malloc(sizeof(double) * (size_t)n);
+  if (!pw || !v) {
+    free(pw);
+    free(v);
+    return -2;
+  }
+  const double a = head_scale[0];
+  for (int r = 0; r < s->rows; ++r) {
+    double ss = 0.0;
+    for (int64_t t = 0; t < n; ++t) {
+      v[t] = act_get(s->act, state, (int64_t)r * n + t);
+      ss += v[t] * v[t];
+    }
+    const double rms = sqrt(ss / (double)n + s->eps_hc);
+    for (int i = 0; i < NSTREAM; ++i) {
+      double acc = 0.0;
+      for (int64_t t = 0; t < n; ++t) acc += (double)w_head[(int64_t)i * n + t] * v[t];
+      const float m = (float)(acc / rms);
+      pw[r * NSTREAM + i] = (float)sigmoid(a * (double)m + (double)head_base[i]);
+    }
+  }
+  free(v);
+  const int rc = or_collapse_norm(s, state, pw, w_norm, x, norm);
+  if (rc == 0 && pre) memcpy(pre, pw, sizeof(float) * (size_t)s->rows * NSTREAM);
+  free(pw);
+  return rc;
+}
+
+/* ---------------------------------------------------------------------------------------------
  * Router logits [ds4 router commit: "the F32 logits matvec"]: logits[e] = f32(W_r[e] . norm). */
 int or_router_logits(const or_shape* s, const void* norm, const float* w_router, float* logits) {
   if (!shape_ok(s) || !norm || !w_router || !logits) return -1;

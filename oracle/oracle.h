@@ -65,6 +65,10 @@ int or_split(const or_shape* s, const float* mixes, const float* hc_scale, const
 /* x, norm [R][H] (act) from the state, pre and w_norm [H] (act). */
 int or_collapse_norm(const or_shape* s, const void* state, const float* pre, const void* w_norm,
                      void* x, void* norm);
+/* Model tail: pre [R][4] (optional), x, norm [R][H] (act) from the state, the head's mix
+ * w_head [4][4H], head_scale [1], head_base [4] and the output norm weight [H] (act); no split. */
+int or_head(const or_shape* s, const void* state, const float* w_head, const float* head_scale,
+            const float* head_base, const void* w_norm, float* pre, void* x, void* norm);
 /* logits [R][E] from norm and w_router [E][H]. */
 int or_router_logits(const or_shape* s, const void* norm, const float* w_router, float* logits);
 /* idx [R][k], weights [R][k] from logits and bias [E]; beta_sorted [R][E] (optional) receives the

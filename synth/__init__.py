@@ -55,6 +55,7 @@ _NP = {F32_NORMAL: np.float32, F32_UNIFORM: np.float32, BF16_NORMAL: np.uint16,
 # tensor tags
 TAG_STATE, TAG_W_MIX, TAG_HC_BASE, TAG_W_NORM, TAG_W_ROUTER, TAG_BIAS = 1, 2, 3, 4, 5, 6
 TAG_GATE, TAG_UP, TAG_DOWN, TAG_GATE_S, TAG_UP_S, TAG_DOWN_S = 7, 8, 9, 10, 11, 12
+TAG_W_HEAD, TAG_HEAD_BASE, TAG_W_OUT_NORM, TAG_ATTN_GAIN = 13, 14, 15, 16
 SHARED_INDEX = 0x80000000
 
 HC_SCALE = (0.12, 0.08, 0.10)
@@ -310,6 +311,43 @@ def dense_specs(cfg: Config, layer: int):
     nb = (E + BIAS_GROUP - 1) // BIAS_GROUP if cfg.grouped_bias else E
     specs["bias"] = (Gen(F32_UNIFORM, key(seed, TAG_BIAS, 0), lo, w), nb, np.float32)
     return specs
+
+
+# the attention half of layer l uses the dense HC tensors (w_mix, hc_scale, hc_base, w_norm) of
+# layer ATTN_LAYER + l, drawn like a layer half's
+ATTN_LAYER = 500
+HEAD_SCALE = 0.12
+
+
+def head_specs(cfg: Config):
+    """Streams of the model-tail head: its 4-row mix, 4 biases and the output norm weight."""
+    seed = cfg.base_seed
+    H = cfg.hidden
+    uni = lambda lo, hi: (float(np.float32(lo)), float(np.float32(np.float32(hi) - np.float32(lo))))
+    lo, w = uni(-1.0, 1.0)
+    specs = {
+        "w_head": (Gen(F32_NORMAL, key(seed, TAG_W_HEAD, 0), normal_c(0.02)), N_STREAMS * N_STREAMS * H,
+                   np.float32),
+        "head_base": (Gen(F32_UNIFORM, key(seed, TAG_HEAD_BASE, 0), lo, w), N_STREAMS, np.float32),
+    }
+    lo, w = uni(0.5, 1.5)
+    specs["w_norm"] = (Gen(_act_uniform(cfg.act), key(seed, TAG_W_OUT_NORM, 0), lo, w), H,
+                       act_np(cfg.act))
+    return specs
+
+
+def head_host(cfg: Config) -> Dict[str, np.ndarray]:
+    out = {name: fill_host(g, n) for name, (g, n, dt) in head_specs(cfg).items()}
+    out["w_head"] = out["w_head"].reshape(N_STREAMS, N_STREAMS * cfg.hidden)
+    out["head_scale"] = np.array([HEAD_SCALE], dtype=np.float32)
+    return out
+
+
+def attn_gain_host(cfg: Config, layer: int) -> np.ndarray:
+    """Per-position gains [H] of the stand-in attention of layer `layer` (uniform in [-1, 1])."""
+    lo, w = float(np.float32(-1.0)), float(np.float32(2.0))
+    return fill_host(Gen(F32_UNIFORM, key(cfg.layer_seed(layer), TAG_ATTN_GAIN, 0), lo, w),
+                     cfg.hidden)
 
 
 def dense_host(cfg: Config, layer: int) -> Dict[str, np.ndarray]:

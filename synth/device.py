@@ -50,6 +50,18 @@ def dense(cfg: synth.Config, layer: int, device="cuda") -> Dict[str, "torch.Tens
     return out
 
 
+def head(cfg: synth.Config, device="cuda") -> Dict[str, "torch.Tensor"]:
+    """w_head, head_scale, head_base, w_norm of the model tail as device tensors (raw storage)."""
+    out = {}
+    for name, (g, n, dt) in synth.head_specs(cfg).items():
+        t = _bytes(n * np.dtype(dt).itemsize, device)
+        _fill(t, g, n)
+        out[name] = t
+    out["head_scale"] = torch.tensor([synth.HEAD_SCALE], dtype=torch.float32,
+                                     device=device).view(torch.uint8)
+    return out
+
+
 def experts(cfg: synth.Config, layer: int, shared: bool, device="cuda",
             n: Optional[int] = None) -> Dict[str, "torch.Tensor"]:
     """Stacked expert matrices: gate, up, down (+ gate_s, up_s, down_s) as byte tensors.

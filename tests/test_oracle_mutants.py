@@ -22,10 +22,22 @@ import oracle
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = ["tests/test_oracle_hc.py", "tests/test_oracle_router.py", "tests/test_oracle_experts.py",
-        "tests/test_oracle_formats.py"]
+        "tests/test_oracle_formats.py", "tests/test_oracle_head.py"]
 
 # name: [(text in oracle.c, replacement), ...]
 MUTANTS = {
+    # model tail: RMS over the H values of one stream instead of the 4H of the row
+    "head_rms_over_one_stream": [("const double rms = sqrt(ss / (double)n + s->eps_hc);",
+                                  "const double rms = sqrt(ss / (double)s->hidden + s->eps_hc);")],
+    # model tail: every pre weight takes the first bias
+    "head_first_bias_only": [("(double)m + (double)head_base[i]);",
+                              "(double)m + (double)head_base[0]);")],
+    # model tail: the head scale dropped
+    "head_scale_dropped": [("pw[r * NSTREAM + i] = (float)sigmoid(a * (double)m +",
+                            "pw[r * NSTREAM + i] = (float)sigmoid(1.0 * (double)m +")],
+    # model tail: head rows read transposed (row i takes the stream-i column block of row 0)
+    "head_rows_transposed": [("acc += (double)w_head[(int64_t)i * n + t] * v[t];",
+                              "acc += (double)w_head[(t % NSTREAM) * n + (t / NSTREAM) + 0 * i] * v[t];")],
     # collapse: gate 3 - i weights stream i
     "collapse_pairing": [("acc += (double)pre[r * NSTREAM + i] *",
                           "acc += (double)pre[r * NSTREAM + (NSTREAM - 1 - i)] *")],
