@@ -244,6 +244,27 @@ mono_status mono_hc_expand(const mono_shape* shape, const void* state, const voi
                            const float* post, const float* comb, const float* w_mix_next,
                            void* new_state, float* carry_out, void* ws, void* stream);
 
+/* The model tail's head weights: its own 4-row mix, one scale, four biases and the output norm
+ * weight. All device pointers, caller-owned. */
+typedef struct {
+  const float* w_head;     /* [4][4H] f32 */
+  const float* head_scale; /* [1] f32 */
+  const float* head_base;  /* [4] f32 */
+  const void* w_norm;      /* [H] act: the output norm weight */
+} mono_head;
+
+/* Model tail [ds4 page, single-box commit: the logits' collapse and the output norm reuse the
+ * collapse without a split; SGLang fused post/pre page, Modifications: the last FFN post is
+ * deferred and closed at the model tail]. From the new state of the last layer half:
+ *   m[i] = (w_head[i] . s) / sqrt(mean(s^2) + eps_hc) over the flattened row s (4H values),
+ *   pre[i] = sigmoid(head_scale m[i] + head_base[i]) (the split's pre half; no post, comb or
+ *   Sinkhorn), x = act(sum_i pre[i] state_i), norm = act(x / sqrt(mean(x^2) + eps_norm) w_norm).
+ *   state [R][4][H] act (read); pre [R][4] f32 and x [R][H] act may be NULL; norm [R][H] act.
+ * Uses shape's rows, hidden, act, eps_hc and eps_norm (the rest must still be a valid shape).
+ * One launch of R workgroups on `stream`; no workspace. */
+mono_status mono_hc_head(const mono_shape* shape, const void* state, const mono_head* head,
+                         float* pre, void* x, void* norm, void* stream);
+
 /* The whole layer half as ONE persistent launch [SGLang mono page, K2; lm-sys page, Layer
  * diagram: mix weights and the shared expert load early, routed weights after routing; vLLM
  * GLM-5 page, Details: residual stream carried across per-layer launches, the epoch advanced

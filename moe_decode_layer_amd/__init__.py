@@ -6,5 +6,5 @@ require a GPU; calling a compute entry point does, and there is no CPU path.
 """
 
 from ._binding import *  # noqa: F401,F403
-from ._binding import (EXPORTS, FMT, LIB_PATH, Experts, Layer, MonoError, Shape, lib,  # noqa: F401
-                       make_experts, make_layer, make_shape, ptr)
+from ._binding import (EXPORTS, FMT, LIB_PATH, Experts, Head, Layer, MonoError, Shape,  # noqa: F401
+                       lib, make_experts, make_head, make_layer, make_shape, ptr)

@@ -26,7 +26,7 @@ EXPORTS = ("mono_workspace_bytes", "mono_workspace_init", "mono_workspace_poll",
            "mono_workspace_set_debug", "mono_workspace_set_trace", "mono_workspace_set_jitter",
            "mono_workspace_tensor", "mono_last_error",
            "mono_grid_size", "mono_hc_mix_collapse", "mono_router_select", "mono_moe_experts",
-           "mono_hc_expand", "mono_ffn_layer", "mono_ffn_layer_static")
+           "mono_hc_expand", "mono_hc_head", "mono_ffn_layer", "mono_ffn_layer_static")
 MONO_STATIC_WS_BYTES = 8 << 20
 MONO_JITTER_MAX_TICKS = 10000
 
@@ -59,6 +59,11 @@ class Layer(ctypes.Structure):
                 ("routed", Experts), ("shared", Experts)]
 
 
+class Head(ctypes.Structure):
+    _fields_ = [("w_head", ctypes.c_void_p), ("head_scale", ctypes.c_void_p),
+                ("head_base", ctypes.c_void_p), ("w_norm", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -87,6 +92,7 @@ def lib() -> ctypes.CDLL:
             "mono_router_select": (I, [SP, P, LP, P, P, P, P, P]),
             "mono_moe_experts": (I, [SP, P, P, P, LP, P, P, P, P, P]),
             "mono_hc_expand": (I, [SP, P, P, P, P, P, P, P, P, P]),
+            "mono_hc_head": (I, [SP, P, ctypes.POINTER(Head), P, P, P, P]),
             "mono_ffn_layer": (I, [SP, LP, P, P, P, P, P, P, P]),
             "mono_ffn_layer_static": (I, [SP, LP, P, P, P, P, P, P]),
         }
@@ -129,6 +135,10 @@ def make_layer(w_mix, hc_scale, hc_base, w_norm, w_router, bias, routed: Experts
                shared: Experts) -> Layer:
     return Layer(ptr(w_mix), ptr(hc_scale), ptr(hc_base), ptr(w_norm), ptr(w_router), ptr(bias),
                  routed, shared)
+
+
+def make_head(w_head, head_scale, head_base, w_norm) -> Head:
+    return Head(ptr(w_head), ptr(head_scale), ptr(head_base), ptr(w_norm))
 
 
 def mono_last_error() -> str:
@@ -203,6 +213,11 @@ def mono_hc_expand(shape, state, block, post, comb, w_mix_next, new_state, carry
                    stream=None) -> None:
     _ok(lib().mono_hc_expand(ctypes.byref(shape), ptr(state), ptr(block), ptr(post), ptr(comb),
                              ptr(w_mix_next), ptr(new_state), ptr(carry_out), ptr(ws), stream))
+
+
+def mono_hc_head(shape, state, head, pre, x, norm, stream=None) -> None:
+    _ok(lib().mono_hc_head(ctypes.byref(shape), ptr(state), ctypes.byref(head), ptr(pre), ptr(x),
+                           ptr(norm), stream))
 
 
 def mono_ffn_layer(shape, layer, w_mix_next, state_in, carry_in, state_out, carry_out, ws,

@@ -14,7 +14,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmonolayer.so")
 ARCH = os.environ.get("MONO_OFFLOAD_ARCH", "gfx950")
 SOURCES = ["mono_launch.hip", "mono_k_f32.hip", "mono_k_bf16.hip", "mono_k_q8.hip",
-           "mono_k_fp4.hip", "mono_api.cpp", "mono_static.hip"]
+           "mono_k_fp4.hip", "mono_api.cpp", "mono_static.hip", "mono_head.hip"]
 
 # Packed-FP32 instructions are disabled for all device code.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-Xclang", "-target-feature",

@@ -24,6 +24,9 @@
 namespace mono {
 int launch_debug(uint32_t* ctl, uint32_t spin, uint32_t fwg, uint32_t fph, void* stream);
 int launch_trace(uint32_t* ctl, uint32_t on, void* stream);
+int launch_head(int act, int rows, int H, float eps_hc, float eps_norm, const void* state,
+                const float* w_head, const float* head_scale, const float* head_base,
+                const void* w_norm, float* pre, void* x, void* norm, void* stream);
 }
 
 namespace {
@@ -492,6 +495,33 @@ mono_status mono_moe_experts(const mono_shape* shape, const void* norm, const in
   if (st == MONO_OK) st = enqueue(K_DOWN, p, shape, rf, sf, grid, stream, "experts down");
   if (st == MONO_OK) g_error.clear();
   return st;
+}
+
+mono_status mono_hc_head(const mono_shape* shape, const void* state, const mono_head* head,
+                         float* pre, void* x, void* norm, void* stream) {
+  Check c;
+  check_shape(c, shape);
+  c.req(head != nullptr, "head is NULL");
+  if (c.code == MONO_OK) {
+    c.ptr(state, "state", 16);
+    c.ptr(head->w_head, "head.w_head", 16);
+    c.ptr(head->head_scale, "head.head_scale");
+    c.ptr(head->head_base, "head.head_base");
+    c.ptr(head->w_norm, "head.w_norm", 16);
+    c.ptr(norm, "norm", 16);
+    if (pre) c.ptr(pre, "pre");
+    if (x) c.ptr(x, "x", 16);
+  }
+  if (c.code != MONO_OK || shape->rows == 0) return c.done();
+  const int rc = launch_head(shape->act, shape->rows, shape->hidden, shape->eps_hc,
+                             shape->eps_norm, state, head->w_head, head->head_scale,
+                             head->head_base, head->w_norm, pre, x, norm, stream);
+  if (rc != 0) {
+    g_error = std::string("hc head: ") + hipGetErrorString((hipError_t)rc);
+    return MONO_E_DEVICE;
+  }
+  g_error.clear();
+  return MONO_OK;
 }
 
 mono_status mono_hc_expand(const mono_shape* shape, const void* state, const void* block,

@@ -367,9 +367,11 @@ def check_selection(got_idx, got_w, ref_idx, ref_w, beta_sorted, k):
     return near
 
 
-def compare_stagewise(cfg: synth.Config, out: Dict[str, np.ndarray], state_h, dense_h,
-                      routed_get, shared_h, w_next_h=None, carry_in=None) -> Dict[str, float]:
-    """Each stage of `out` (GPU) against the oracle fed the GPU's inputs to that stage."""
+def compare_pre_side(cfg: synth.Config, out: Dict[str, np.ndarray], state_h, dense_h,
+                     carry_in=None) -> Dict[str, float]:
+    """The HC pre side of `out` (mixes, pre, post, comb, x, norm) against the oracle fed the
+    GPU's inputs to each stage: the mix from the state or from the carry, the split from the
+    GPU's mixes, the collapse and norm from the GPU's pre weights."""
     s = oracle.shape_of(cfg)
     act = cfg.act
     rep = {}
@@ -385,6 +387,15 @@ def compare_stagewise(cfg: synth.Config, out: Dict[str, np.ndarray], state_h, de
     x, norm = oracle.collapse_norm(s, state_h, out["pre"], dense_h["w_norm"])
     rep["x"] = check_bf16("x", out["x"], x, act)
     rep["norm"] = check_bf16("norm", out["norm"], norm, act)
+    return rep
+
+
+def compare_stagewise(cfg: synth.Config, out: Dict[str, np.ndarray], state_h, dense_h,
+                      routed_get, shared_h, w_next_h=None, carry_in=None) -> Dict[str, float]:
+    """Each stage of `out` (GPU) against the oracle fed the GPU's inputs to that stage."""
+    s = oracle.shape_of(cfg)
+    act = cfg.act
+    rep = compare_pre_side(cfg, out, state_h, dense_h, carry_in)
     lg = oracle.router_logits(s, out["norm"], dense_h["w_router"])
     rep["logits"] = check_f32("logits", out["logits"], lg)
     idx, w, beta = oracle.select(s, out["logits"], dense_h["bias"])

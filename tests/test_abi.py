@@ -173,3 +173,15 @@ def test_race_shaker_limit_is_checked_before_any_device_work():
     with pytest.raises(B.MonoError) as e:
         B.mono_workspace_set_jitter(P256 + 16, 100, 7)
     assert "ws is not 256-byte aligned" in e.value.message
+
+
+def test_model_tail_checks_every_pointer():
+    s = shape(rows=2)
+    head = B.make_head(None, P16, None, P16 + 2)
+    with pytest.raises(B.MonoError) as e:
+        B.mono_hc_head(s, P16 + 4, head, None, None, None)
+    msg = e.value.message
+    for part in ("state is not 16-byte aligned", "head.w_head is NULL", "head.head_base is NULL",
+                 "head.w_norm is not 16-byte aligned", "norm is NULL"):
+        assert part in msg, (part, msg)
+    B.mono_hc_head(shape(rows=0), P16, B.make_head(P16, P16, P16, P16), None, None, P16)
