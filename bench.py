@@ -119,6 +119,57 @@ class Workload:
         return dict(wall_s=wall, span_ms=span_ms, dur_ms=dur_ms, bytes=np.array(nbytes))
 
 
+def seam_timings(cfg, reps: int = 50) -> dict:
+    """Mean launch time of the attention half's seam calls and of the model tail at one row,
+    each on its own inputs resident in HBM: the attention pre side from the previous FFN half's
+    carry (mono_hc_mix_collapse), its post side with the carry for the FFN half
+    (mono_hc_expand), and the tail (mono_hc_head: head mix, collapse, output norm)."""
+    import torch
+    import moe_decode_layer_amd as mono
+    from moe_decode_layer_amd import host
+    import synth
+    import synth.device as sdev
+    R, H = cfg.rows, cfg.hidden
+    ab = 4 if cfg.act == "f32" else 2
+    shape = host.shape_of(cfg)
+    ws = torch.zeros(mono.mono_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    mono.mono_workspace_init(ws, shape, host.current_stream())
+    attn = sdev.dense(cfg, synth.ATTN_LAYER)
+    ffn_mix = sdev.dense(cfg, 0)["w_mix"]
+    L = mono.make_layer(attn["w_mix"], attn["hc_scale"], attn["hc_base"], attn["w_norm"], None,
+                        None, mono.Experts(), mono.Experts())
+    ht = sdev.head(cfg)
+    head = mono.make_head(ht["w_head"], ht["head_scale"], ht["head_base"], ht["w_norm"])
+    st = sdev.state(cfg, 0)
+    f32 = lambda n: torch.zeros(n, dtype=torch.float32, device="cuda")
+    raw = lambda n: torch.zeros(n, dtype=torch.uint8, device="cuda")
+    carry = torch.rand(R * 25, device="cuda") + 1.0
+    mixes, pre, post, comb = f32(R * 24), f32(R * 4), f32(R * 4), f32(R * 16)
+    x, norm, blk = raw(R * H * ab), raw(R * H * ab), raw(R * H * ab)
+    new, carry2 = raw(R * 4 * H * ab), f32(R * 25)
+    s = host.current_stream()
+    calls = {
+        "attn_pre_from_carry": lambda: mono.mono_hc_mix_collapse(
+            shape, st, L, carry, mixes, pre, post, comb, x, norm, ws, s),
+        "attn_post_with_carry": lambda: mono.mono_hc_expand(
+            shape, st, blk, post, comb, ffn_mix, new, carry2, ws, s),
+        "model_tail": lambda: mono.mono_hc_head(shape, st, head, pre, x, norm, s),
+    }
+    out = {"workload": cfg.name + ": attention-half seam and model tail", "rows": R}
+    for name, fn in calls.items():
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        out[name + "_us"] = a.elapsed_time(b) * 1e3 / reps
+    return out
+
+
 class ChainWorkload:
     """The 8-layer-half chain at 1 row: one step is 8 fused launches, layer l taking the carry of
     layer l - 1 (its mix matvec skipped) and producing the next one's, the last with no carry.
@@ -371,6 +422,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-rows6", action="store_true", help="skip the 6- and 8-row workloads")
     ap.add_argument("--no-chain", action="store_true", help="skip the 8-layer chain")
+    ap.add_argument("--no-seam", action="store_true",
+                    help="skip the attention-half seam and model-tail timings")
     ap.add_argument("--no-drafts", action="store_true",
                     help="skip the draft routing shapes (128 experts top-3, 256 experts top-6)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -452,6 +505,9 @@ def main():
             del wx
             torch.cuda.empty_cache()
         extra["drafts"] = drafts
+    if not args.no_seam:
+        extra["seam"] = seam_timings(cfg1)
+        log("  seam:", json.dumps(extra["seam"]))
     if not args.no_chain:
         cfg5 = synth.CONFIGS[5]
         wc = ChainWorkload(cfg5)
