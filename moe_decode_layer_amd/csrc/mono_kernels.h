@@ -469,6 +469,8 @@ struct Smem {
   int routed_next; /* next routed gate/up task of this workgroup (fused launch) */
   int down_next;   /* next down block of the current staged group (fused launch, several rows),
                       or next down task of the one-row flow */
+  int em_q0, em_q1, em_u1; /* several rows: this workgroup's down stretch [q0, q1) and the end
+                              of its first staged group, found with the plan */
   int stage_state[kMaxUnion + 1]; /* one-row flow: item staged? 0 no, 1 being staged, 2 yes,
                                      3 its hidden rows did not arrive */
   int nU;
@@ -1430,9 +1432,9 @@ __device__ __forceinline__ void load_selection(const Params& p, Smem& sm) {
  * is the shared expert (every row). Built by wave 0 alone from a bitmap of the selected
  * experts (LDS operations of one wave complete in order); every wave sees it after the
  * __syncthreads at the end. */
-__device__ __forceinline__ void ph_plan(const Params& p, Smem& sm) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x, R = p.R, K = p.K, RK = p.R * p.K;
+__device__ __forceinline__ void plan_wave(const Params& p, Smem& sm) {
+  {
+    const int lane = threadIdx.x & 63, R = p.R, K = p.K, RK = p.R * p.K;
     constexpr int NW = kMaxExperts / 32;
     if (lane < NW) sm.ubits[lane] = 0u;
     for (int q = lane; q < RK; q += 64) {
@@ -1471,6 +1473,11 @@ __device__ __forceinline__ void ph_plan(const Params& p, Smem& sm) {
       sm.nU = nU;
     }
   }
+}
+
+/* plan_wave by wave 0, then a workgroup barrier. */
+__device__ __forceinline__ void ph_plan(const Params& p, Smem& sm) {
+  if (threadIdx.x < 64) plan_wave(p, sm);
   __syncthreads();
 }
 
@@ -2017,25 +2024,45 @@ __device__ __forceinline__ int down_item(const Params& p, const Smem& sm, int k)
 }
 
 /* End of the group of items [k0, end): as many as fit the staging area next to used0 bytes and
- * count0 rows already listed, at most max_items. */
+ * count0 rows already listed, at most max_items. Each wave computes it on its own, 64 items at a
+ * time (one per lane, inclusive prefix sums of bytes and rows, the first item that overflows by
+ * ballot), so no lane waits on a chain of LDS reads; the result is uniform. */
 __device__ __forceinline__ int down_group_end(const Params& p, const Smem& sm, int k0, size_t ab,
                                               int max_items, size_t used0 = 0, int count0 = 0) {
-  const int nU = sm.nU, n_items = nU + (p.Is > 0 ? 1 : 0);
-  int k = k0, count = count0;
-  size_t used = used0;
-  while (k < n_items && k - k0 < max_items) {
-    const int item = down_item(p, sm, k);
-    const int inter = item == nU ? p.Is : p.I;
-    const int rows = __popc(sm.umask[item]);
-    const size_t need = (size_t)rows * inter * ab;
-    /* the first item always fits an empty area; rows already staged (used0) may leave none */
-    if ((k > k0 || count0 > 0) && (used + need > (size_t)kLdsHidBytes || count + rows > kMaxStaged))
-      break;
-    used += need;
-    count += rows;
-    ++k;
+  const int nU = sm.nU, n_items = nU + (p.Is > 0 ? 1 : 0), lane = threadIdx.x & 63;
+  const int kend = min(n_items, k0 + max_items);
+  uint32_t used = (uint32_t)used0;
+  int count = count0;
+  for (int c0 = k0; c0 < kend; c0 += 64) {
+    const int k = c0 + lane;
+    uint32_t need = 0u;
+    int rows = 0;
+    if (k < kend) {
+      const int item = down_item(p, sm, k);
+      rows = __popc(sm.umask[item]);
+      need = (uint32_t)((size_t)rows * (item == nU ? p.Is : p.I) * ab);
+    }
+    uint32_t pn = need;
+    int pr = rows;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t tn = __shfl_up(pn, d);
+      const int tr = __shfl_up(pr, d);
+      if (lane >= d) {
+        pn += tn;
+        pr += tr;
+      }
+    }
+    /* the first item always fits an empty area; rows already listed (count0) may leave none */
+    const bool first_item = k == k0 && count0 == 0;
+    const bool over = k < kend && !first_item &&
+                      (used + pn > (uint32_t)kLdsHidBytes || count + pr > kMaxStaged);
+    const uint64_t ov = __ballot(over);
+    if (ov != 0ull) return c0 + (int)__builtin_ctzll(ov);
+    used += __shfl(pn, 63);
+    count += __shfl(pr, 63);
   }
-  return k;
+  return kend;
 }
 
 /* Hidden-position slice of the workgroup for the down projections and the expand. */
@@ -2101,10 +2128,10 @@ __device__ __forceinline__ void slice_store(const Params& p, const Slice& c, Sme
  * that uses it), in item-major
  * order, the source of the hidden row (routed [R][K][I] or shared [R][Is]), its LDS offset and
  * length in 16-byte units, and sm.voff. One wave scans the items 64 at a time. */
-__device__ __forceinline__ void stage_list(const Params& p, Smem& sm, int first, int last,
-                                           size_t ab, bool lead_shared = false) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x, nU = sm.nU;
+__device__ __forceinline__ void stage_list_wave(const Params& p, Smem& sm, int first, int last,
+                                                size_t ab, bool lead_shared = false) {
+  {
+    const int lane = threadIdx.x & 63, nU = sm.nU;
     /* with lead_shared the shared expert (position 0) comes before positions [first, last) */
     const int lead = lead_shared ? 1 : 0, n = lead + (last - first);
     int nv = 0;
@@ -2149,6 +2176,12 @@ __device__ __forceinline__ void stage_list(const Params& p, Smem& sm, int first,
     }
     if (lane == 0) sm.nv = nv;
   }
+}
+
+/* stage_list_wave by wave 0, then a workgroup barrier. */
+__device__ __forceinline__ void stage_list(const Params& p, Smem& sm, int first, int last,
+                                           size_t ab, bool lead_shared = false) {
+  if (threadIdx.x < 64) stage_list_wave(p, sm, first, last, ab, lead_shared);
   __syncthreads();
 }
 
@@ -2777,26 +2810,69 @@ __device__ __forceinline__ uint32_t em_cost(int n) { return n == 1 ? 2u : n == 2
 
 /* Workgroup b's stretch [q0, q1) of the nU * nqi routed blocks: the list is cut at the blocks
  * whose cost prefix first reaches b / grid and (b + 1) / grid of the total, so every workgroup
- * gets the same cost and the stretches tile the list. */
+ * gets the same cost and the stretches tile the list. One wave, one lane per item
+ * (nU <= kMaxUnion = 128: two items per lane), prefix sums and ballots; 32-bit arithmetic (the
+ * total cost is at most 10 nqi nU, and times the grid it stays below 2^32). */
 __device__ __forceinline__ void em_stretch(const Smem& sm, int nqi, int& q0, int& q1) {
-  const int nU = sm.nU, G = gridDim.x, b = blockIdx.x;
-  uint64_t W = 0;
-  for (int u = 0; u < nU; ++u) W += (uint64_t)nqi * em_cost(__popc(sm.umask[u]));
-  const uint64_t c0 = W * b / G, c1 = W * (b + 1) / G;
-  q0 = q1 = nU * nqi;
-  bool f0 = false, f1 = false;
-  uint64_t P = 0;
-  for (int u = 0; u < nU && !f1; ++u) {
-    const uint64_t w = em_cost(__popc(sm.umask[u])), Pn = P + (uint64_t)nqi * w;
-    if (!f0 && c0 < Pn) {
-      q0 = u * nqi + (int)((c0 - P + w - 1) / w);
-      f0 = true;
+  static_assert(kMaxUnion <= 128, "em_stretch covers two items per lane");
+  const int nU = sm.nU, G = gridDim.x, b = blockIdx.x, lane = threadIdx.x & 63;
+  uint32_t w[2], incl[2], carry = 0u;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int u = lane + 64 * h;
+    w[h] = u < nU ? em_cost(__popc(sm.umask[u])) : 0u;
+    uint32_t x = w[h] * (uint32_t)nqi;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t t = __shfl_up(x, d);
+      if (lane >= d) x += t;
     }
-    if (c1 < Pn) {
-      q1 = u * nqi + (int)((c1 - P + w - 1) / w);
-      f1 = true;
+    incl[h] = carry + x;
+    carry += __shfl(x, 63);
+  }
+  const uint32_t W = carry;
+  const uint32_t c0 = W * (uint32_t)b / (uint32_t)G, c1 = W * (uint32_t)(b + 1) / (uint32_t)G;
+  /* the first item whose inclusive prefix exceeds c; the block is u nqi + ceil((c - P) / w) */
+  auto cut = [&](uint32_t c) -> int {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int u = lane + 64 * h;
+      const uint64_t hit = __ballot(u < nU && c < incl[h]);
+      if (hit != 0ull) {
+        const int src = (int)__builtin_ctzll(hit);
+        const uint32_t wu = (uint32_t)__shfl((int)w[h], src);
+        const uint32_t P = (uint32_t)__shfl((int)incl[h], src) - wu * (uint32_t)nqi;
+        return (64 * h + src) * nqi + (int)((c - P + wu - 1u) / wu);
+      }
     }
-    P = Pn;
+    return nU * nqi;
+  };
+  q0 = cut(c0);
+  q1 = cut(c1);
+}
+
+/* After the plan, by wave 0 while the other waves start the gate/up phase (which leaves these
+ * LDS fields alone): the workgroup's down stretch, the end of its first staged group and that
+ * group's staging list, so that the down phase starts with the copy. The other waves read them
+ * after the barrier at the start of ph_down_em. */
+template <int ACT, int RFMT>
+__device__ __forceinline__ void em_prepare(const Params& p, Smem& sm) {
+  const int nqi = p.H / Wide<RFMT>::DG, off = p.Is > 0 ? 1 : 0;
+  const size_t ab = ACT == F32 ? 4 : 2;
+  int q0, q1;
+  em_stretch(sm, nqi, q0, q1);
+  const int u = q0 / nqi, uend = q1 > q0 ? (q1 - 1) / nqi + 1 : u;
+  const bool has_sh = p.Is > 0 && slice_of(p).nh > 0;
+  const int u1 = u < uend ? down_group_end(p, sm, u + off, ab, uend - u,
+                                           has_sh ? (size_t)p.R * p.Is * ab : 0, has_sh ? p.R : 0) -
+                                off
+                          : u;
+  stage_list_wave(p, sm, u + off, u1 + off, ab, has_sh);
+  if ((threadIdx.x & 63) == 0) {
+    sm.em_q0 = q0;
+    sm.em_q1 = q1;
+    sm.em_u1 = u1;
+    sm.down_next = 0;
   }
 }
 
@@ -2810,9 +2886,10 @@ __device__ __forceinline__ bool ph_down_em(const Params& p, Smem& sm, uint32_t h
   const Slice c = slice_of(p);
   SliceRegs sreg;
   slice_prefetch<ACT>(p, c, sreg);
-  /* this workgroup's stretch of routed blocks */
-  int q0, q1;
-  em_stretch(sm, nqi, q0, q1);
+  /* this workgroup's stretch of routed blocks, from em_prepare (wave 0): every wave is done
+   * with its gate/up rows after this barrier, and sees what wave 0 wrote */
+  __syncthreads();
+  const int q0 = sm.em_q0, q1 = sm.em_q1;
   int u = q0 / nqi;
   const int uend = q1 > q0 ? (q1 - 1) / nqi + 1 : u;
   /* the first staged group holds the shared expert's hidden rows (for this workgroup's slice of
@@ -2822,13 +2899,15 @@ __device__ __forceinline__ bool ph_down_em(const Params& p, Smem& sm, uint32_t h
   bool first = true;
   while (u < uend || (first && has_sh)) {
     const bool with_sh = first && has_sh;
-    const size_t sh_bytes = with_sh ? (size_t)R * p.Is * ab : 0;
-    const int u1 = u < uend ? down_group_end(p, sm, u + off, ab, uend - u, sh_bytes,
-                                             with_sh ? R : 0) - off
-                            : u;
-    if (!first) __syncthreads(); /* the previous items' tasks are done with the staging area */
-    if (tid == 0) sm.down_next = 0; /* visible after stage_list's barrier */
-    stage_list(p, sm, u + off, u1 + off, ab, with_sh);
+    int u1;
+    if (first) {
+      u1 = sm.em_u1; /* listed by em_prepare; sm.down_next is zero */
+    } else {
+      u1 = u < uend ? down_group_end(p, sm, u + off, ab, uend - u) - off : u;
+      __syncthreads(); /* the previous items' tasks are done with the staging area */
+      if (tid == 0) sm.down_next = 0; /* visible after stage_list's barrier */
+      stage_list(p, sm, u + off, u1 + off, ab, false);
+    }
     if (!stage_copy<ACT>(p, sm, true, htag)) return false;
     if (first) {
       slice_store(p, c, sm, sreg);
@@ -3201,6 +3280,12 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   stamp(p, tr, 7);
   shake(p, sm, 7);
   ph_plan(p, sm);
+  /* several rows: wave 0 prepares the down phase while the others start the gate/up rows; it
+   * reads the plan only after the plan's barrier (lanes of one wave exchange LDS values only
+   * across a barrier: without one the compiler may schedule one lane's load before another
+   * lane's store) */
+  if constexpr (RMAX > 1)
+    if (threadIdx.x < 64) em_prepare<ACT, RFMT>(p, sm);
   stamp(p, tr, 8);
   shake(p, sm, 8);
   ph_gateup_routed<ACT, RFMT, RMAX>(p, sm, htag, hskip);
