@@ -471,6 +471,8 @@ struct Smem {
                       or next down task of the one-row flow */
   int em_q0, em_q1, em_u1; /* several rows: this workgroup's down stretch [q0, q1) and the end
                               of its first staged group, found with the plan */
+  int lg_ready;   /* one row: wave 0 has gathered the logits (or given up waiting) */
+  int plan_ready; /* one row: 0 not yet, 1 the plan is built, 2 the logits did not arrive */
   int stage_state[kMaxUnion + 1]; /* one-row flow: item staged? 0 no, 1 being staged, 2 yes,
                                      3 its hidden rows did not arrive */
   int nU;
@@ -1315,7 +1317,9 @@ __device__ __forceinline__ bool select_row(const Params& p, Smem& sm, int r, boo
   const int lane = threadIdx.x & 63, E = p.E, K = p.K;
   uint32_t kh[PER], kl[PER];
   float sv[PER], zs[PER];
-  if (!gather_logits<PER>(p, sm, r, check, tag, zs)) return false;
+  const bool gathered = gather_logits<PER>(p, sm, r, check, tag, zs);
+  if (lane == 0) __hip_atomic_store(&sm.lg_ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (!gathered) return false;
   stamp(p, sm.trace_on != 0, 24);
 #pragma unroll
   for (int c = 0; c < PER; ++c) {
@@ -1380,6 +1384,31 @@ __device__ __forceinline__ void select_rows(const Params& p, Smem& sm, bool writ
 /* Select, part 2 (after a __syncthreads that follows part 1): normalised, clamped and scaled
  * routing weights. Returns false (after reporting once) when some row's logits did not arrive
  * in time. */
+/* The weights of select_finish, without its barrier: threads 0 .. R - 1 (all in wave 0 when
+ * R <= 64). Returns false (after reporting once) when some row's logits did not arrive. */
+__device__ __forceinline__ bool select_finish_nobar(const Params& p, Smem& sm, bool write_out) {
+  const int tid = threadIdx.x, K = p.K;
+  if (sm.sel_ok == 0) {
+    if (tid == 0) report_timeout(p, PH_ROUTER);
+    return false;
+  }
+  if (tid < p.R) {
+    const int r = tid;
+    float sum = 0.0f;
+    for (int j = 0; j < K; ++j) sum += sm.sel_s[r][j];
+    const float c = fmaxf(sum, 6.103515625e-05f); /* 2^-14 */
+    for (int j = 0; j < K; ++j) {
+      const float w = (sm.sel_s[r][j] / c) * p.rho;
+      sm.sel_w[r][j] = w;
+      if (write_out) {
+        p.idx[r * K + j] = sm.sel_e[r][j];
+        p.weights[r * K + j] = w;
+      }
+    }
+  }
+  return true;
+}
+
 __device__ __forceinline__ bool select_finish(const Params& p, Smem& sm, bool write_out) {
   const int tid = threadIdx.x, K = p.K;
   if (sm.sel_ok == 0) {
@@ -3238,6 +3267,8 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   for (int i = threadIdx.x; i <= kMaxUnion; i += kBlock) sm.stage_state[i] = 0;
   if (threadIdx.x == 0) {
     sm.sel_ok = 1;
+    sm.lg_ready = 0;
+    sm.plan_ready = 0;
     sm.shared_next = 0;
     sm.routed_next = 0;
     sm.down_next = 0;
@@ -3263,11 +3294,46 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   const uint32_t htag = (uint32_t)(sm.epoch % 65535u) + 1u;
   const bool hskip = sm.skip_phase == PH_GATEUP; /* fault injection: store no hidden rows */
   if (RMAX == 1) {
-    /* one row: wave 0 selects while the other waves take the shared expert's rows */
+    /* one row: wave 0 selects while the other waves take the shared expert's rows, which they
+     * start once wave 0 has gathered the logits: their loads would otherwise queue ahead of its
+     * polls (bounded wait; wave 0 sets the flag whether or not the logits arrived) */
     select_rows(p, sm, blockIdx.x == 0, true, tag);
+    if (threadIdx.x < 64) {
+      /* wave 0 finishes the select and builds the plan without waiting for the other waves'
+       * shared rows, then publishes it through sm.plan_ready (1 ready, 2 the logits did not
+       * arrive). The fences order the lanes' LDS accesses: lane 0 wrote the selection. */
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+      const bool ok = select_finish_nobar(p, sm, blockIdx.x == 0);
+      stamp(p, tr, 7);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+      if (ok) plan_wave(p, sm);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (threadIdx.x == 0)
+        __hip_atomic_store(&sm.plan_ready, ok ? 1 : 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      stamp(p, tr, 8);
+    } else {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__hip_atomic_load(&sm.lg_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0 &&
+             __builtin_amdgcn_s_memrealtime() - t0 <= sm.spin)
+        __builtin_amdgcn_s_sleep(2);
+    }
     stamp(p, tr, 6);
     ph_gateup_shared_claim<ACT, SFMT, RMAX>(p, sm, htag, hskip);
     stamp(p, tr, 5);
+    /* bounded wait for the plan (usually ready by now). Wave 0 sets the flag at most a few
+     * microseconds after its own bounded gather ends, so with twice the limit every wave sees
+     * the same value; on a failed select all waves return. */
+    {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      int st;
+      while ((st = __hip_atomic_load(&sm.plan_ready, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_WORKGROUP)) == 0 &&
+             __builtin_amdgcn_s_memrealtime() - t0 <= 2ull * sm.spin)
+        __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      if (st != 1) return;
+    }
+    shake(p, sm, 8);
   } else {
     /* several rows: most waves select, so the shared rows go first, while the logits arrive */
     ph_gateup_shared_claim<ACT, SFMT, RMAX>(p, sm, htag, hskip);
@@ -3275,19 +3341,20 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
     select_rows(p, sm, blockIdx.x == 0, true, tag);
     stamp(p, tr, 6);
   }
-  __syncthreads();
-  if (!select_finish(p, sm, blockIdx.x == 0)) return;
-  stamp(p, tr, 7);
-  shake(p, sm, 7);
-  ph_plan(p, sm);
-  /* several rows: wave 0 prepares the down phase while the others start the gate/up rows; it
-   * reads the plan only after the plan's barrier (lanes of one wave exchange LDS values only
-   * across a barrier: without one the compiler may schedule one lane's load before another
-   * lane's store) */
-  if constexpr (RMAX > 1)
+  if constexpr (RMAX > 1) {
+    __syncthreads();
+    if (!select_finish(p, sm, blockIdx.x == 0)) return;
+    stamp(p, tr, 7);
+    shake(p, sm, 7);
+    ph_plan(p, sm);
+    /* wave 0 prepares the down phase while the others start the gate/up rows; it reads the
+     * plan only after the plan's barrier (lanes of one wave exchange LDS values only across a
+     * barrier or fence: without one the compiler may schedule one lane's load before another
+     * lane's store) */
     if (threadIdx.x < 64) em_prepare<ACT, RFMT>(p, sm);
-  stamp(p, tr, 8);
-  shake(p, sm, 8);
+    stamp(p, tr, 8);
+    shake(p, sm, 8);
+  }
   ph_gateup_routed<ACT, RFMT, RMAX>(p, sm, htag, hskip);
   stamp(p, tr, 9);
   shake(p, sm, 9);
