@@ -1345,7 +1345,11 @@ __device__ __forceinline__ bool select_row(const Params& p, Smem& sm, int r, boo
       key_cx(kh[c], kl[c], sv[c], kh[c + 1], kl[c + 1], sv[c + 1]);
   for (int j = 0; j < K; ++j) {
     const uint32_t mh = wave_max_u32(kh[0]);
-    const uint32_t ml = wave_max_u32(kh[0] == mh ? kl[0] : 0u);
+    /* the low word decides only between lanes that share the highest score */
+    const uint64_t top = __ballot(kh[0] == mh);
+    const uint32_t ml = __popcll(top) == 1
+                            ? (uint32_t)__builtin_amdgcn_readlane((int)kl[0], (int)__builtin_ctzll(top))
+                            : wave_max_u32(kh[0] == mh ? kl[0] : 0u);
     const bool win = kh[0] == mh && kl[0] == ml;
     const uint64_t who = __ballot(win);
     const float s_win = readlane(sv[0], (int)__builtin_ctzll(who));
@@ -1462,6 +1466,27 @@ __device__ __forceinline__ void load_selection(const Params& p, Smem& sm) {
  * experts (LDS operations of one wave complete in order); every wave sees it after the
  * __syncthreads at the end. */
 __device__ __forceinline__ void plan_wave(const Params& p, Smem& sm) {
+  if (p.R == 1) {
+    /* one row: its k experts are distinct, so the plan is their ascending order; lane q < k
+     * ranks expert sel_e[0][q] among them (same result as the bitmap walk below) */
+    const int lane = threadIdx.x & 63, K = p.K;
+    const int e = lane < K ? sm.sel_e[0][lane] : 0x7FFFFFFF;
+    int rank = 0;
+    for (int t = 0; t < K; ++t) rank += __builtin_amdgcn_readlane(e, t) < e ? 1 : 0;
+    for (int q = lane; q < (K + 1) * kMaxRows; q += 64) sm.uslot[q / kMaxRows][q % kMaxRows] = -1;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup"); /* the -1s land before the slots */
+    if (lane < K) {
+      sm.U[rank] = e;
+      sm.umask[rank] = 1u;
+      sm.uslot[rank][0] = (int8_t)lane;
+    }
+    if (lane == 0) {
+      sm.umask[K] = 1u;
+      sm.uslot[K][0] = (int8_t)K;
+      sm.nU = K;
+    }
+    return;
+  }
   {
     const int lane = threadIdx.x & 63, R = p.R, K = p.K, RK = p.R * p.K;
     constexpr int NW = kMaxExperts / 32;
