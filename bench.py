@@ -333,7 +333,7 @@ def cpu_baseline(cfg1, cfg6, budget_s: float):
 # ---- HBM traffic from rocprofv3 counters -------------------------------------------------
 
 KERNEL_SOURCES = ["mono_kernels.h", "mono_internal.h", "mono_launch.hip", "mono_k_bf16.hip"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_ffn_layer_bf16_r1_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_ffn_layer_traffic.md")
 
 
 def kernel_source_hash() -> str:
