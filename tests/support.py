@@ -14,9 +14,10 @@ Comparison rules (written out here and used by every parity test):
     the tensor's rms (smaller ones are near-cancellations; the contract still bounds them).
   * SwiGLU hidden values: an element outside these rules is accepted only when it equals (within
     one step) the result of another admissible rounding of its gate or up sum (check_hidden).
-  * free-running (end-to-end) comparison: the same rules up to the hidden rows; after them an
-    error budget adds the first-order effect of the measured input differences (see
-    compare_end_to_end).
+  * free-running (end-to-end) comparison: the same rules for every bf16 tensor up to the
+    hidden rows; the logits, the routing weights and every tensor after the hidden rows also
+    get an error budget, the first-order effect of the measured differences of their inputs
+    (see compare_end_to_end).
 Each stage is compared with the oracle fed the GPU's own inputs to that stage (teacher
 forcing), so one rounding flip upstream does not cascade; compare_end_to_end also compares
 every output with the oracle run free from the same input when no selection rests on a near
