@@ -27,6 +27,8 @@ LIB = os.environ.get("MONO_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 F32, BF16, Q8_0, MXFP4 = 0, 1, 2, 3
 FMT = {"f32": F32, "bf16": BF16, "q8_0": Q8_0, "mxfp4": MXFP4}
+# activation quantisation of the expert matvecs: none, or MXFP8 for the MXFP4 matrices
+AQ = {"none": 0, "mxfp8": 1}
 N_MIX = 24
 
 
@@ -46,7 +48,7 @@ class Shape(ctypes.Structure):
                 ("top_k", ctypes.c_int), ("inter", ctypes.c_int), ("shared_inter", ctypes.c_int),
                 ("act", ctypes.c_int), ("sinkhorn_iters", ctypes.c_int),
                 ("routed_scale", ctypes.c_double), ("eps_hc", ctypes.c_double),
-                ("eps_norm", ctypes.c_double)]
+                ("eps_norm", ctypes.c_double), ("act_quant", ctypes.c_int)]
 
 
 class Mat(ctypes.Structure):
@@ -92,6 +94,10 @@ def lib():
         L.or_e2m1_to_f64.restype = ctypes.c_double
         L.or_e8m0_to_f64.argtypes = [ctypes.c_uint8]
         L.or_e8m0_to_f64.restype = ctypes.c_double
+        L.or_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        L.or_e4m3_to_f64.restype = ctypes.c_double
+        L.or_mxfp8_quant.argtypes = [P, ctypes.c_int, P, P]
+        L.or_mxfp8_quant.restype = ctypes.c_int
         L.or_mat_elem.argtypes = [ctypes.POINTER(Mat), ctypes.c_int64, ctypes.c_int64,
                                   ctypes.c_int64]
         L.or_mat_elem.restype = ctypes.c_double
@@ -123,15 +129,16 @@ def _check(rc: int, what: str) -> None:
 
 
 def make_shape(rows, hidden, n_experts, top_k, inter, shared_inter, act, routed_scale,
-               sinkhorn_iters=20, eps_hc=1e-6, eps_norm=1e-6) -> Shape:
+               sinkhorn_iters=20, eps_hc=1e-6, eps_norm=1e-6, act_quant="none") -> Shape:
     return Shape(rows, hidden, n_experts, top_k, inter, shared_inter,
-                 F32 if act == "f32" else BF16, sinkhorn_iters, routed_scale, eps_hc, eps_norm)
+                 F32 if act == "f32" else BF16, sinkhorn_iters, routed_scale, eps_hc, eps_norm,
+                 AQ[act_quant])
 
 
 def shape_of(cfg, rows: Optional[int] = None) -> Shape:
     return make_shape(cfg.rows if rows is None else rows, cfg.hidden, cfg.n_experts, cfg.top_k,
                       cfg.inter, cfg.shared_inter, cfg.act, cfg.routed_scale, cfg.sinkhorn_iters,
-                      cfg.eps_hc, cfg.eps_norm)
+                      cfg.eps_hc, cfg.eps_norm, getattr(cfg, "act_quant", "none"))
 
 
 def _act_dtype(s: Shape):
@@ -288,6 +295,19 @@ def e2m1_to_f64(c: int) -> float:
 
 def e8m0_to_f64(e: int) -> float:
     return float(lib().or_e8m0_to_f64(e))
+
+
+def e4m3_to_f64(c: int) -> float:
+    return float(lib().or_e4m3_to_f64(c))
+
+
+def mxfp8_quant(v) -> tuple:
+    """MXFP8 quantisation of a vector (length a multiple of 32): (E4M3 codes, e8m0 scales)."""
+    x = np.ascontiguousarray(v, dtype=np.float64)
+    codes = np.zeros(x.size, np.uint8)
+    scales = np.zeros(x.size // 32, np.uint8)
+    _check(lib().or_mxfp8_quant(_p(x), x.size, _p(codes), _p(scales)), "mxfp8_quant")
+    return codes, scales
 
 
 def mat_elem(fmt: str, values, scales, k: int, row: int, col: int) -> float:

@@ -167,6 +167,99 @@ static double mat_row_dot(const or_mat* m, int64_t k, int64_t row, const double*
   }
 }
 
+/* ---------------------------------------------------------------------------------------------
+ * MXFP8 activations for MXFP4 experts [vLLM "[ROCm][Perf][GLM-5] Fused sparse-layer decode via
+ * AITER MonoKernel", Details, Numerics: the activations entering the MXFP4 experts are quantised
+ * to MXFP8]. The page names the format only. READING: the conversion is the one of the OCP
+ * Microscaling (MX) specification v1.0 with E4M3 elements:
+ *   - blocks of 32 consecutive values along the contraction dimension share one e8m0 scale 2^X,
+ *     X = floor(log2(max |v|)) - 8 (8 is the exponent of the largest E4M3 power of two),
+ *     clamped to [-127, 127]; an all-zero block takes X = -127;
+ *   - each value becomes the E4M3 number nearest to v / 2^X, ties to the even mantissa, and a
+ *     magnitude above 448 (the largest finite E4M3) becomes 448.
+ * The quantised vector replaces the input of each expert matrix stored in MXFP4: the norm row
+ * for gate and up, the hidden row for down. The stored tensors (norm, h) are not changed.
+ *
+ * E4M3 (OFP8): sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+ * subnormals m / 8 * 2^-6; S.1111.111 is NaN; there are no infinities. */
+double or_e4m3_to_f64(uint8_t c) {
+  const unsigned e = (c >> 3) & 0xFu, m = c & 7u;
+  if (e == 15u && m == 7u) return NAN;
+  const double mag = e == 0u ? ldexp((double)m, -9) : ldexp(8.0 + (double)m, (int)e - 10);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+/* E4M3 code of a value already rounded to E4M3 precision and within +-448. */
+static uint8_t e4m3_encode(double r) {
+  const uint8_t sign = (r < 0.0 || (r == 0.0 && signbit(r))) ? 0x80u : 0u;
+  const double a = fabs(r);
+  if (a < ldexp(1.0, -6)) return (uint8_t)(sign | (uint8_t)(a / ldexp(1.0, -9)));
+  int e2;
+  (void)frexp(a, &e2); /* a = f 2^e2, f in [0.5, 1): floor(log2 a) = e2 - 1 */
+  const int e = e2 - 1;
+  const unsigned m = (unsigned)(a / ldexp(1.0, e - 3)) - 8u;
+  return (uint8_t)(sign | (unsigned)((e + 7) << 3) | m);
+}
+
+int or_mxfp8_quant(const double* v, int n, uint8_t* codes, uint8_t* scales) {
+  if (!v || !codes || !scales || n < 0 || n % QBLOCK) return -1;
+  for (int b = 0; b < n / QBLOCK; ++b) {
+    const double* x = v + (int64_t)b * QBLOCK;
+    double amax = 0.0;
+    for (int i = 0; i < QBLOCK; ++i)
+      if (fabs(x[i]) > amax) amax = fabs(x[i]);
+    int X = -127;
+    if (amax > 0.0) {
+      int e2;
+      (void)frexp(amax, &e2);
+      X = (e2 - 1) - 8;
+      if (X < -127) X = -127;
+      if (X > 127) X = 127;
+    }
+    scales[b] = (uint8_t)(X + 127);
+    for (int i = 0; i < QBLOCK; ++i) {
+      const double t = ldexp(x[i], -X); /* exact */
+      const double a = fabs(t);
+      double q; /* E4M3 spacing at a */
+      if (a < ldexp(1.0, -6)) {
+        q = ldexp(1.0, -9);
+      } else {
+        int e2;
+        (void)frexp(a, &e2);
+        q = ldexp(1.0, (e2 - 1) - 3);
+      }
+      double r = nearbyint(t / q) * q; /* default rounding mode: nearest, ties to even */
+      if (r > 448.0) r = 448.0;
+      if (r < -448.0) r = -448.0;
+      if (r == 0.0) r = copysign(0.0, t);
+      codes[(int64_t)b * QBLOCK + i] = e4m3_encode(r);
+    }
+  }
+  return 0;
+}
+
+/* v[0 .. n) replaced by its MXFP8 round trip: code value times the block's scale. */
+static int mxfp8_round_trip(double* v, int n) {
+  uint8_t* c = (uint8_t*)malloc((size_t)n + (size_t)n / QBLOCK + 1);
+  if (!c) return -2;
+  uint8_t* sc = c + n;
+  int rc = or_mxfp8_quant(v, n, c, sc);
+  if (rc == 0)
+    for (int i = 0; i < n; ++i) v[i] = or_e4m3_to_f64(c[i]) * or_e8m0_to_f64(sc[i / QBLOCK]);
+  free(c);
+  return rc;
+}
+
+/* The input a matrix sees: v itself, or its MXFP8 round trip (in vq) when the activations of
+ * MXFP4 experts are quantised. */
+static const double* matrix_input(const or_shape* s, const or_mat* m, const double* v, double* vq,
+                                  int n, int* rc) {
+  if (s->act_quant != OR_AQ_MXFP8 || m->fmt != OR_MXFP4) return v;
+  memcpy(vq, v, sizeof(double) * (size_t)n);
+  *rc = mxfp8_round_trip(vq, n);
+  return vq;
+}
+
 static int mat_ok(const or_mat* m) {
   if (!m->values) return 0;
   if ((m->fmt == OR_Q8_0 || m->fmt == OR_MXFP4) && !m->scales) return 0;
@@ -177,7 +270,8 @@ static int shape_ok(const or_shape* s) {
   return s && s->rows >= 0 && s->hidden > 0 && s->n_experts > 0 && s->top_k > 0 &&
          s->top_k <= s->n_experts && s->inter > 0 && s->shared_inter >= 0 &&
          (s->act == OR_F32 || s->act == OR_BF16) && s->sinkhorn_iters >= 0 &&
-         s->hidden % QBLOCK == 0 && s->inter % QBLOCK == 0 && s->shared_inter % QBLOCK == 0;
+         s->hidden % QBLOCK == 0 && s->inter % QBLOCK == 0 && s->shared_inter % QBLOCK == 0 &&
+         (s->act_quant == OR_AQ_NONE || s->act_quant == OR_AQ_MXFP8);
 }
 
 static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
@@ -429,13 +523,20 @@ int or_expert_hidden(const or_shape* s, int inter, const or_expert* ex, const vo
                      void* h) {
   if (!shape_ok(s) || !ex || !norm_row || !h || !mat_ok(&ex->gate) || !mat_ok(&ex->up)) return -1;
   const int64_t H = s->hidden;
-  double* v = (double*)malloc(sizeof(double) * H);
+  double* v = (double*)malloc(sizeof(double) * H * 3);
   if (!v) return -2;
   for (int64_t c = 0; c < H; ++c) v[c] = act_get(s->act, norm_row, c);
+  int rc = 0;
+  const double* vg = matrix_input(s, &ex->gate, v, v + H, (int)H, &rc);
+  const double* vu = matrix_input(s, &ex->up, v, v + 2 * H, (int)H, &rc);
+  if (rc) {
+    free(v);
+    return rc;
+  }
 #pragma omp parallel for schedule(static)
   for (int i = 0; i < inter; ++i) {
-    float gf = (float)mat_row_dot(&ex->gate, H, i, v);
-    float uf = (float)mat_row_dot(&ex->up, H, i, v);
+    float gf = (float)mat_row_dot(&ex->gate, H, i, vg);
+    float uf = (float)mat_row_dot(&ex->up, H, i, vu);
     double g = (s->act == OR_F32) ? (double)gf : or_bf16_to_f64(or_f32_to_bf16(gf));
     double u = (s->act == OR_F32) ? (double)uf : or_bf16_to_f64(or_f32_to_bf16(uf));
     act_put(s->act, h, i, g / (1.0 + exp(-g)) * u);
@@ -449,11 +550,17 @@ static int expert_down(const or_shape* s, int inter, const or_expert* ex, const 
                        float* y) {
   if (!mat_ok(&ex->down)) return -1;
   const int64_t H = s->hidden;
-  double* v = (double*)malloc(sizeof(double) * inter);
+  double* v = (double*)malloc(sizeof(double) * inter * 2);
   if (!v) return -2;
   for (int i = 0; i < inter; ++i) v[i] = act_get(s->act, h, i);
+  int rc = 0;
+  const double* vd = matrix_input(s, &ex->down, v, v + inter, inter, &rc);
+  if (rc) {
+    free(v);
+    return rc;
+  }
 #pragma omp parallel for schedule(static)
-  for (int64_t c = 0; c < H; ++c) y[c] = (float)mat_row_dot(&ex->down, inter, c, v);
+  for (int64_t c = 0; c < H; ++c) y[c] = (float)mat_row_dot(&ex->down, inter, c, vd);
   free(v);
   return 0;
 }

@@ -29,6 +29,9 @@ extern "C" {
 #endif
 
 enum { OR_F32 = 0, OR_BF16 = 1, OR_Q8_0 = 2, OR_MXFP4 = 3 };
+/* Activation quantisation for the expert matvecs: none, or MXFP8 (E4M3 values, e8m0 scale per
+ * 32) for every matrix stored in MXFP4. */
+enum { OR_AQ_NONE = 0, OR_AQ_MXFP8 = 1 };
 
 typedef struct {
   int rows;         /* R */
@@ -41,6 +44,7 @@ typedef struct {
   int sinkhorn_iters;
   double routed_scale; /* rho */
   double eps_hc, eps_norm;
+  int act_quant;       /* OR_AQ_NONE or OR_AQ_MXFP8 */
 } or_shape;
 
 /* One [rows][k] weight matrix. values: f32 | bf16 bits | int8 | packed e2m1 pairs (low nibble =
@@ -94,6 +98,9 @@ uint16_t or_f32_to_bf16(float f);
 double or_f16_to_f64(uint16_t h);
 double or_e2m1_to_f64(unsigned code);
 double or_e8m0_to_f64(uint8_t e);
+double or_e4m3_to_f64(uint8_t c);
+/* MXFP8 quantisation of v[0 .. n) (n a multiple of 32): E4M3 codes [n] and e8m0 scales [n/32]. */
+int or_mxfp8_quant(const double* v, int n, uint8_t* codes, uint8_t* scales);
 /* Element (row, col) of a matrix with k columns, exactly, in f64. */
 double or_mat_elem(const or_mat* m, int64_t k, int64_t row, int64_t col);
 

@@ -189,6 +189,7 @@ class Config:
     grouped_bias: bool = False
     zero_rows: tuple = ()
     layers: int = 1
+    act_quant: str = "none"  # "mxfp8": activations of the MXFP4 experts quantised to MXFP8
 
     @property
     def base_seed(self) -> int:
@@ -222,6 +223,10 @@ CONFIGS: Dict[int, Config] = {
               FMT_BF16, FMT_BF16, FMT_BF16, 2.5),
     9: Config(9, "MoE half, 256 experts top-6, 6 rows, Q8_0 experts", 6, 5120, 256, 6, 2048, 2048,
               FMT_BF16, FMT_Q8_0, FMT_Q8_0, 2.5),
+    # workload 4 with the activations of the MXFP4 experts quantised to MXFP8 (E4M3, e8m0 per 32)
+    10: Config(10, "V4.1-like MoE half, 8 rows, MXFP4 routed with MXFP8 activations + bf16 shared, "
+               "zero row", 8, 5120, 256, 8, 2048, 2048, FMT_BF16, FMT_MXFP4, FMT_BF16, 2.5,
+               grouped_bias=True, zero_rows=(7,), act_quant="mxfp8"),
 }
 DRAFT_CONFIGS = (6, 7, 8, 9)
 

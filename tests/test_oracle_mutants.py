@@ -22,7 +22,7 @@ import oracle
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = ["tests/test_oracle_hc.py", "tests/test_oracle_router.py", "tests/test_oracle_experts.py",
-        "tests/test_oracle_formats.py", "tests/test_oracle_head.py"]
+        "tests/test_oracle_formats.py", "tests/test_oracle_head.py", "tests/test_oracle_mxfp8.py"]
 
 # name: [(text in oracle.c, replacement), ...]
 MUTANTS = {
@@ -71,10 +71,25 @@ MUTANTS = {
     "weights_from_biased": [("float w = (float)((double)sc[c[j].e] / cl);",
                              "float w = (float)((double)c[j].beta / cl);")],
     # gate and up swapped
-    "gate_up_swapped": [("float gf = (float)mat_row_dot(&ex->gate, H, i, v);",
-                         "float gf = (float)mat_row_dot(&ex->up, H, i, v);"),
-                        ("float uf = (float)mat_row_dot(&ex->up, H, i, v);",
-                         "float uf = (float)mat_row_dot(&ex->gate, H, i, v);")],
+    "gate_up_swapped": [("float gf = (float)mat_row_dot(&ex->gate, H, i, vg);",
+                         "float gf = (float)mat_row_dot(&ex->up, H, i, vu);"),
+                        ("float uf = (float)mat_row_dot(&ex->up, H, i, vu);",
+                         "float uf = (float)mat_row_dot(&ex->gate, H, i, vg);")],
+    # MXFP8: shared exponent from emax 7 instead of 8
+    "mxfp8_emax_7": [("X = (e2 - 1) - 8;", "X = (e2 - 1) - 7;")],
+    # MXFP8: no clamp at the largest finite E4M3
+    "mxfp8_no_saturation": [("if (r > 448.0) r = 448.0;", "")],
+    # MXFP8: ties rounded away from zero
+    "mxfp8_ties_away": [("double r = nearbyint(t / q) * q;", "double r = round(t / q) * q;")],
+    # MXFP8: the down projection sees the unquantised hidden row
+    "mxfp8_down_unquantised": [("y[c] = (float)mat_row_dot(&ex->down, inter, c, vd);",
+                                "y[c] = (float)mat_row_dot(&ex->down, inter, c, v);")],
+    # MXFP8: the up projection sees the unquantised norm row
+    "mxfp8_up_unquantised": [("float uf = (float)mat_row_dot(&ex->up, H, i, vu);",
+                              "float uf = (float)mat_row_dot(&ex->up, H, i, v);")],
+    # MXFP8: the block maximum taken without the magnitude (negative maxima ignored)
+    "mxfp8_signed_max": [("if (fabs(x[i]) > amax) amax = fabs(x[i]);",
+                          "if (x[i] > amax) amax = x[i];")],
     # RMSNorm mean over 4 H
     "norm_mean_over_4h": [("double den = sqrt(ss / (double)H + s->eps_norm);",
                            "double den = sqrt(ss / (double)(4 * H) + s->eps_norm);")],
