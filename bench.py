@@ -7,6 +7,7 @@ carry of the next layer half's mix sums, as ONE persistent launch, with inputs r
 Headline workload: the V4.1-like layer half at 1 row with bf16 experts (hidden 5120, 256
 experts top-8, inter 2048, shared inter 2048). The 6-row Q8_0 and the 8-row MXFP4 (bf16 shared,
 one zero row) workloads are measured in the same run and reported under "rows6" and "rows8",
+the 8-row workload with the MXFP4 experts' activations quantised to MXFP8 under "rows8_mxfp8",
 and the chain of 8 bf16 layer halves (each taking the previous one's carry) under "chain8". Steps rotate over `--copies` independent weight copies and 64
 seeded input states, so routing changes every step and no weight is re-read from the 256 MB
 last-level cache; each step's algorithmic bytes count every distinct selected expert once.
@@ -478,12 +479,13 @@ def main():
     torch.cuda.empty_cache()
     extra = {}
     if not args.no_rows6:
-        for key, ci in (("rows6", 3), ("rows8", 4)):
+        for key, ci in (("rows6", 3), ("rows8", 4), ("rows8_mxfp8", 10)):
             cfgx = synth.CONFIGS[ci]
             wx = Workload(cfgx, args.copies)
             rx = summarize(wx.run(args.steps, args.warmup), cfgx)
             log("  %s:" % key, json.dumps(rx))
-            extra[key] = dict(workload=cfgx.name, rows=cfgx.rows, steps_per_s=rx["steps_per_s"],
+            extra[key] = dict(workload=cfgx.name, rows=cfgx.rows, act_quant=cfgx.act_quant,
+                              steps_per_s=rx["steps_per_s"],
                               launch_us_median=rx["launch_us_median"],
                               launch_us_mean=rx["launch_us_mean"],
                               achieved_gbs=rx["achieved_gbs"],

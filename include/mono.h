@@ -74,6 +74,17 @@ typedef enum {
  *   114688 bytes, rows * max(inter, shared_inter) * ab <= 81920 bytes and
  *   max(inter, shared_inter) * ab <= 16384 bytes, and the slice of hidden positions one
  *   workgroup expands must fit its LDS on the current device (MONO_E_UNSUPPORTED otherwise). */
+/* Activation quantisation of the expert matrix-vector products [vLLM "[ROCm][Perf][GLM-5] Fused
+ * sparse-layer decode via AITER MonoKernel", Details, Numerics: the activations entering the
+ * MXFP4 experts are quantised to MXFP8]. With MONO_AQ_MXFP8 the input of every matrix stored in
+ * MXFP4 (the norm row for gate and up, the hidden row for down) is replaced by its MXFP8 round
+ * trip, the OCP MX v1.0 conversion: per block of 32 values along the contraction, the shared
+ * exponent X = floor(log2 max|v|) - 8 clamped to [-127, 127], each value the E4M3 number nearest
+ * to v / 2^X (ties to even, magnitudes above 448 clamped to 448), times 2^X. Matrices in other
+ * formats see the unquantised activations; the norm and hidden rows written out are unchanged.
+ * Used by mono_moe_experts, mono_ffn_layer and mono_ffn_layer_static; the other calls ignore it. */
+typedef enum { MONO_AQ_NONE = 0, MONO_AQ_MXFP8 = 1 } mono_act_quant;
+
 typedef struct {
   int rows;         /* R: decode rows (tokens) in the step */
   int hidden;       /* H */
@@ -87,6 +98,8 @@ typedef struct {
   int sinkhorn_iters; /* Sinkhorn iterations for comb (20 in the workloads) */
   float eps_hc;       /* epsilon inside the mix RMS (1e-6) */
   float eps_norm;     /* epsilon inside the collapse RMSNorm (1e-6) */
+  int act_quant;      /* mono_act_quant: MONO_AQ_MXFP8 quantises the activations entering the
+                         MXFP4 experts (routed.fmt must be MONO_MXFP4) */
 } mono_shape;
 
 /* One expert set: n experts (n = E routed, n = 1 shared), each gate [inter][H], up [inter][H],

@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libmonolayer.so")
 
 MONO_F32, MONO_BF16, MONO_Q8_0, MONO_MXFP4 = 0, 1, 2, 3
 FMT = {"f32": MONO_F32, "bf16": MONO_BF16, "q8_0": MONO_Q8_0, "mxfp4": MONO_MXFP4}
+MONO_AQ_NONE, MONO_AQ_MXFP8 = 0, 1
+AQ = {"none": MONO_AQ_NONE, "mxfp8": MONO_AQ_MXFP8}
 MONO_OK, MONO_E_INVAL, MONO_E_UNSUPPORTED, MONO_E_DEVICE, MONO_E_TIMEOUT = 0, -1, -2, -3, -4
 (MONO_T_MIXES, MONO_T_PRE, MONO_T_POST, MONO_T_COMB, MONO_T_X, MONO_T_NORM, MONO_T_LOGITS,
  MONO_T_IDX, MONO_T_WEIGHTS, MONO_T_H_ROUTED, MONO_T_H_SHARED, MONO_T_SHARED, MONO_T_ROUTED,
@@ -43,7 +45,8 @@ class Shape(ctypes.Structure):
                 ("n_experts", ctypes.c_int), ("top_k", ctypes.c_int), ("inter", ctypes.c_int),
                 ("shared_inter", ctypes.c_int), ("act", ctypes.c_int),
                 ("routed_scale", ctypes.c_float), ("sinkhorn_iters", ctypes.c_int),
-                ("eps_hc", ctypes.c_float), ("eps_norm", ctypes.c_float)]
+                ("eps_hc", ctypes.c_float), ("eps_norm", ctypes.c_float),
+                ("act_quant", ctypes.c_int)]
 
 
 class Experts(ctypes.Structure):
@@ -120,10 +123,10 @@ def _ok(status: int) -> None:
 
 def make_shape(rows, hidden, n_experts, top_k, inter, shared_inter, act="bf16",
                routed_scale=1.0, sinkhorn_iters=20, eps_hc=1e-6, eps_norm=1e-6,
-               n_streams=4) -> Shape:
+               n_streams=4, act_quant="none") -> Shape:
     return Shape(rows, hidden, n_streams, n_experts, top_k, inter, shared_inter,
                  FMT[act] if isinstance(act, str) else act, routed_scale, sinkhorn_iters,
-                 eps_hc, eps_norm)
+                 eps_hc, eps_norm, AQ[act_quant] if isinstance(act_quant, str) else act_quant)
 
 
 def make_experts(fmt, gate, up, down, gate_s=None, up_s=None, down_s=None) -> Experts:

@@ -96,6 +96,8 @@ void check_shape(Check& c, const mono_shape* s) {
     c.fail(MONO_E_INVAL, "sinkhorn_iters=%d not in [0, 1000]", s->sinkhorn_iters);
   if (!std::isfinite(s->routed_scale)) c.fail(MONO_E_INVAL, "routed_scale is not finite");
   if (!(s->eps_hc >= 0.0f) || !(s->eps_norm >= 0.0f)) c.fail(MONO_E_INVAL, "eps_hc / eps_norm must be >= 0");
+  if (s->act_quant != MONO_AQ_NONE && s->act_quant != MONO_AQ_MXFP8)
+    c.fail(MONO_E_INVAL, "act_quant=%d (must be MONO_AQ_NONE or MONO_AQ_MXFP8)", s->act_quant);
   if (act_ok(s->act) && s->rows > 0 && s->hidden > 0) {
     const size_t ab = s->act == MONO_F32 ? 4 : 2;
     const size_t wide = (size_t)(s->inter > s->shared_inter ? s->inter : s->shared_inter);
@@ -124,6 +126,9 @@ void check_formats(Check& c, const mono_shape* s, const mono_layer* L, bool rout
   };
   if (routed) one(L->routed, "routed");
   if (shared && s->shared_inter > 0) one(L->shared, "shared");
+  if (routed && s->act_quant == MONO_AQ_MXFP8 && L->routed.fmt != MONO_MXFP4)
+    c.fail(MONO_E_UNSUPPORTED, "act_quant MONO_AQ_MXFP8 needs routed.fmt MONO_MXFP4 (routed.fmt=%d)",
+           (int)L->routed.fmt);
 }
 
 void check_experts(Check& c, const mono_shape* s, const mono_experts& x, const char* name,
@@ -199,6 +204,7 @@ Params base_params(const mono_shape* s, const mono_layer* L, void* ws, int grid)
   p.R = s->rows; p.H = s->hidden; p.E = s->n_experts; p.K = s->top_k; p.I = s->inter;
   p.Is = s->shared_inter; p.iters = s->sinkhorn_iters; p.nslice = grid;
   p.rho = s->routed_scale; p.eps_hc = s->eps_hc; p.eps_norm = s->eps_norm;
+  p.aq8 = s->act_quant == MONO_AQ_MXFP8 ? 1 : 0;
   if (L) {
     p.w_mix = L->w_mix; p.hc_scale = L->hc_scale; p.hc_base = L->hc_base; p.w_norm = L->w_norm;
     p.w_router = L->w_router; p.bias = L->bias;

@@ -60,6 +60,7 @@ struct Mat {
 struct Params {
   int R, H, E, K, I, Is, iters, nslice;
   float rho, eps_hc, eps_norm;
+  int aq8; /* MXFP8 round trip of the activations entering the MXFP4 experts (routed is MXFP4) */
   uint32_t jitter, jseed; /* race shaker of the fused launch: largest delay in ticks (0 = off) */
   /* weights */
   const float* w_mix;

@@ -98,6 +98,52 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
   return __uint_as_float(e << 23);
 }
 
+/* MXFP8 round trip of a value v of a block whose shared exponent is X [vLLM "[ROCm][Perf][GLM-5]
+ * Fused sparse-layer decode via AITER MonoKernel", Details, Numerics: activations of the MXFP4
+ * experts quantised to MXFP8]. READING: the OCP MX v1.0 conversion with E4M3 elements: v / 2^X
+ * rounded to the nearest E4M3 number (3 mantissa bits; below 2^-6 the subnormal spacing 2^-9),
+ * ties to even, magnitudes above 448 clamped to 448, then times 2^X. Every step is exact in f32
+ * except the one rounding (rintf rounds to nearest even). */
+__device__ __forceinline__ float mx8_rt(float v, int X) {
+  const float t = ldexpf(v, -X);
+  const uint32_t eb = __float_as_uint(t) >> 23 & 0xFFu; /* biased exponent of |t| */
+  const int qe = eb < 121u ? -9 : (int)eb - 130;         /* log2 of the E4M3 spacing at |t| */
+  float r = ldexpf(rintf(ldexpf(t, -qe)), qe);
+  r = fminf(fmaxf(r, -448.0f), 448.0f);
+  return ldexpf(r, X);
+}
+
+/* MXFP8 round trip, in place, of one block of 32 bf16 values (64 bytes of LDS). The shared
+ * exponent is X = floor(log2 max|v|) - 8, clamped to [-127, 127] (bf16 magnitudes order as
+ * integers, and the exponent field of the largest is floor(log2) + 127). An all-zero block is
+ * left as it is. The results are exact in bf16 (4 significant bits times a power of two). */
+__device__ __forceinline__ void mx8_block_lds(uint8_t* b) {
+  uint4* q = reinterpret_cast<uint4*>(b);
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = q[i];
+    w[4 * i] = v.x;
+    w[4 * i + 1] = v.y;
+    w[4 * i + 2] = v.z;
+    w[4 * i + 3] = v.w;
+  }
+  uint32_t mx = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    mx = max(mx, w[j] & 0x7FFFu);
+    mx = max(mx, (w[j] >> 16) & 0x7FFFu);
+  }
+  if (mx == 0) return;
+  int X = (int)(mx >> 7) - 127 - 8;
+  X = X < -127 ? -127 : (X > 127 ? 127 : X);
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    w[j] = f2bf2(mx8_rt(bf2f(w[j] & 0xFFFFu), X), mx8_rt(bf2f(w[j] >> 16), X));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+}
+
 /* c + a.lo * b.lo + a.hi * b.hi for packed bf16 pairs. */
 __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -1032,6 +1078,16 @@ __device__ __forceinline__ void act_rows_ptrs(const Params& p, const Smem& sm,
 #pragma unroll
   for (int r = 0; r < RMAX; ++r)
     arow[r] = sm.big + (size_t)(r < p.R ? r : 0) * p.H * (ACT == F32 ? 4 : 2);
+}
+
+/* MXFP8 round trip, in place, of the R bf16 activation rows at the start of sm.big (blocks of 32
+ * along H, one per thread at a time). Whole workgroup; the caller places the barriers. */
+template <int ACT>
+__device__ __forceinline__ void mx8_act_rows(const Params& p, Smem& sm) {
+  if constexpr (ACT == BF16) {
+    const int nb = p.R * p.H / 32;
+    for (int b = threadIdx.x; b < nb; b += kBlock) mx8_block_lds(sm.big + (size_t)b * 64);
+  }
 }
 
 /* ------------------------------------------------------------------------------------------
@@ -2245,7 +2301,8 @@ __device__ __forceinline__ void stage_list(const Params& p, Smem& sm, int first,
  * check, a chunk whose tags are not yet `tag` is loaded again (bounded wait); on expiry the
  * function reports once and returns false for the whole workgroup. */
 template <int ACT>
-__device__ __forceinline__ bool stage_copy(const Params& p, Smem& sm, bool check, uint32_t tag) {
+__device__ __forceinline__ bool stage_copy(const Params& p, Smem& sm, bool check, uint32_t tag,
+                                           bool mx_shared) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int TB = ACT == F32 ? 8 : 4; /* tagged bytes per value */
   constexpr int EPC = ACT == F32 ? 4 : 8; /* values per 16-byte LDS chunk */
@@ -2333,6 +2390,16 @@ __device__ __forceinline__ bool stage_copy(const Params& p, Smem& sm, bool check
     if (threadIdx.x == 0) report_timeout(p, PH_GATEUP);
     return false;
   }
+  /* MXFP8 activations: the hidden rows entering MXFP4 down projections (the routed ones, and the
+   * shared one when mx_shared) take their round trip in place */
+  if (ACT == BF16 && p.aq8) {
+    for (int u = wave; u < nv; u += kWaves) {
+      if ((sm.vsrc[u] & kHidShared) && !mx_shared) continue;
+      const int nblk = sm.vlen[u] / 4;
+      for (int b = lane; b < nblk; b += 64) mx8_block_lds(sm.big + (size_t)sm.vdst[u] * 16 + b * 64);
+    }
+    __syncthreads();
+  }
   return true;
 }
 
@@ -2381,7 +2448,7 @@ __device__ __forceinline__ bool flow_fits(const Params& p, const Smem& sm, size_
  * dropping the tags, each 16-byte chunk polled (bounded) until its tags are `tag`. */
 template <int ACT>
 __device__ __forceinline__ bool flow_stage(const Params& p, Smem& sm, int item, uint32_t off,
-                                           uint32_t tag) {
+                                           uint32_t tag, bool mx) {
   const int lane = threadIdx.x & 63, nU = sm.nU;
   constexpr int TB = ACT == F32 ? 8 : 4, EPC = ACT == F32 ? 4 : 8;
   const bool sh = item == nU;
@@ -2437,6 +2504,13 @@ __device__ __forceinline__ bool flow_stage(const Params& p, Smem& sm, int item, 
       *reinterpret_cast<uint4*>(sm.big + off + (size_t)c * 16) = v;
     }
   }
+  if (ACT == BF16 && mx) {
+    /* MXFP8 round trip of the staged row (its down projection is MXFP4); the lanes read chunks
+     * other lanes wrote, so the fences order the LDS accesses */
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    for (int b = lane; b < inter / 32; b += 64) mx8_block_lds(sm.big + off + (size_t)b * 64);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  }
   return __ballot(!ok) == 0ull;
 }
 
@@ -2489,7 +2563,8 @@ __device__ __forceinline__ bool ph_down_flow(const Params& p, Smem& sm, uint32_t
     const int st = __builtin_amdgcn_readfirstlane(atomicCAS(&sm.stage_state[k], 0, 1));
     if (st == 0) {
       const uint32_t off = flow_off(p, k, ab);
-      const bool got = ok && flow_stage<ACT>(p, sm, it, off, htag);
+      const bool got =
+          ok && flow_stage<ACT>(p, sm, it, off, htag, p.aq8 && (it != nU || SFMT == FP4));
       if ((threadIdx.x & 63) == 0) {
         sm.voff[it][__builtin_ctz(sm.umask[it])] = (uint16_t)(off / 16);
         __hip_atomic_store(&sm.stage_state[k], got ? 2 : 3, __ATOMIC_RELEASE,
@@ -2557,7 +2632,7 @@ __device__ __forceinline__ bool ph_down(const Params& p, Smem& sm, uint32_t htag
         have_pre = true;
       }
     }
-    if (!stage_copy<ACT>(p, sm, FUSED, htag)) return false;
+    if (!stage_copy<ACT>(p, sm, FUSED, htag, SFMT == FP4)) return false;
     if (FUSED && k0 == 0) {
       slice_store(p, c, sm, sreg);
       stamp(p, sm.trace_on != 0, 21);
@@ -2962,7 +3037,7 @@ __device__ __forceinline__ bool ph_down_em(const Params& p, Smem& sm, uint32_t h
       if (tid == 0) sm.down_next = 0; /* visible after stage_list's barrier */
       stage_list(p, sm, u + off, u1 + off, ab, false);
     }
-    if (!stage_copy<ACT>(p, sm, true, htag)) return false;
+    if (!stage_copy<ACT>(p, sm, true, htag, SFMT == FP4)) return false;
     if (first) {
       slice_store(p, c, sm, sreg);
       stamp(p, sm.trace_on != 0, 21);
@@ -3214,7 +3289,18 @@ __global__ void __launch_bounds__(kBlock) k_gateup(Params p) {
   load_act_rows<ACT>(p.norm_in, p.R, p.H, sm);
   load_selection(p, sm);
   ph_plan(p, sm);
+  /* MXFP8 activations: the MXFP4 experts see the round trip of the norm rows, the others the
+   * rows themselves (the routed experts are MXFP4 in this mode) */
+  if (p.aq8 && SFMT == FP4) {
+    mx8_act_rows<ACT>(p, sm);
+    __syncthreads();
+  }
   ph_gateup_shared<ACT, SFMT, RMAX>(p, sm);
+  if (p.aq8 && SFMT != FP4) {
+    __syncthreads();
+    mx8_act_rows<ACT>(p, sm);
+    __syncthreads();
+  }
   ph_gateup_routed<ACT, RFMT, RMAX>(p, sm, 0u, false);
 }
 
@@ -3315,6 +3401,13 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   stamp(p, tr, 4);
   shake(p, sm, 4);
   ph_sinkhorn(p, sm, blockIdx.x == 0); /* comb is needed only by the expand */
+  /* MXFP8 activations with an MXFP4 shared expert: every expert sees the round trip of the norm
+   * rows, so it replaces them once the router has read them */
+  if (p.aq8 && SFMT == FP4) {
+    __syncthreads();
+    mx8_act_rows<ACT>(p, sm);
+    __syncthreads();
+  }
   /* hidden rows carry a 16-bit tag of this launch (never 0, the value the init leaves) */
   const uint32_t htag = (uint32_t)(sm.epoch % 65535u) + 1u;
   const bool hskip = sm.skip_phase == PH_GATEUP; /* fault injection: store no hidden rows */
@@ -3358,6 +3451,13 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       if (st != 1) return;
     }
+    /* MXFP8 activations, shared expert not MXFP4: the routed rows see the round trip of the
+     * norm row, after every wave is done with the shared rows */
+    if (p.aq8 && SFMT != FP4) {
+      __syncthreads();
+      mx8_act_rows<ACT>(p, sm);
+      __syncthreads();
+    }
     shake(p, sm, 8);
   } else {
     /* several rows: most waves select, so the shared rows go first, while the logits arrive */
@@ -3371,6 +3471,9 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
     if (!select_finish(p, sm, blockIdx.x == 0)) return;
     stamp(p, tr, 7);
     shake(p, sm, 7);
+    /* MXFP8 activations, shared expert not MXFP4: the round trip of the norm rows for the
+     * routed gate/up (every wave is done with the shared rows; ph_plan's barrier follows) */
+    if (p.aq8 && SFMT != FP4) mx8_act_rows<ACT>(p, sm);
     ph_plan(p, sm);
     /* wave 0 prepares the down phase while the others start the gate/up rows; it reads the
      * plan only after the plan's barrier (lanes of one wave exchange LDS values only across a

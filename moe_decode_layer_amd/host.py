@@ -19,7 +19,8 @@ from . import _binding as B
 def shape_of(cfg, rows: Optional[int] = None) -> B.Shape:
     return B.make_shape(cfg.rows if rows is None else rows, cfg.hidden, cfg.n_experts,
                         cfg.top_k, cfg.inter, cfg.shared_inter, cfg.act, cfg.routed_scale,
-                        cfg.sinkhorn_iters, cfg.eps_hc, cfg.eps_norm)
+                        cfg.sinkhorn_iters, cfg.eps_hc, cfg.eps_norm,
+                        act_quant=getattr(cfg, "act_quant", "none"))
 
 
 def experts_struct(fmt: str, t: Optional[Dict]) -> B.Experts:

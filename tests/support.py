@@ -255,7 +255,19 @@ def _bf16_choices(v: float, slack: float):
 FLIP_REL = 2.0 ** -16
 
 
-def check_hidden(name, got, ref, act, norm, rows) -> float:
+_E4M3 = None
+
+
+def mx8_round_trip(x) -> np.ndarray:
+    """The MXFP8 round trip of an activation row (the oracle's quantiser and E4M3 decode)."""
+    global _E4M3
+    if _E4M3 is None:
+        _E4M3 = np.array([oracle.e4m3_to_f64(c) for c in range(256)])
+    codes, scales = oracle.mxfp8_quant(x)
+    return _E4M3[codes] * np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32)
+
+
+def check_hidden(name, got, ref, act, norm, rows, aq="none") -> float:
     """SwiGLU hidden values h = bf16(silu(g) u) with g = bf16(W_g . x) and u = bf16(W_u . x): the
     contract and step rules, except that an element outside them is accepted when it is within
     one bf16 step of h computed from some admissible rounding of g and u. Admissible: the exact
@@ -277,6 +289,8 @@ def check_hidden(name, got, ref, act, norm, rows) -> float:
         fmt, t, arow = rows(ix[:-1])
         i = ix[-1]
         x = nrm[arow]
+        if aq == "mxfp8" and fmt == "mxfp4":  # the input the MXFP4 matrices see
+            x = mx8_round_trip(x)
         wg = support_dequant_row(fmt, t["gate"], t.get("gate_s"), i)
         wu = support_dequant_row(fmt, t["up"], t.get("up_s"), i)
         gv, uv = float(wg @ x), float(wu @ x)
@@ -405,10 +419,12 @@ def compare_stagewise(cfg: synth.Config, out: Dict[str, np.ndarray], state_h, de
     experts = {int(e): routed_get(int(e)) for e in np.unique(gidx)}
     m = oracle.moe(s, out["norm"], gidx, gw, cfg.routed_fmt, experts, cfg.shared_fmt, shared_h)
     rep["h_routed"] = check_hidden("h_routed", out["h_routed"], m["h_routed"], act, out["norm"],
-                                   lambda rj: (cfg.routed_fmt, experts[int(gidx[rj])], rj[0]))
+                                   lambda rj: (cfg.routed_fmt, experts[int(gidx[rj])], rj[0]),
+                                   cfg.act_quant)
     if cfg.shared_inter > 0:
         rep["h_shared"] = check_hidden("h_shared", out["h_shared"], m["h_shared"], act,
-                                       out["norm"], lambda r_: (cfg.shared_fmt, shared_h, r_[0]))
+                                       out["norm"], lambda r_: (cfg.shared_fmt, shared_h, r_[0]),
+                                       cfg.act_quant)
     # down projections, routed sum, shared rounding and block: the oracle fed the GPU's hidden
     # rows (one rounding flip in h does not cascade)
     f = oracle.moe(s, None, gidx, gw, cfg.routed_fmt, experts, cfg.shared_fmt, shared_h,
@@ -499,11 +515,25 @@ def compare_end_to_end(cfg: synth.Config, out: Dict[str, np.ndarray], state_h, d
     getx = lambda e: cache.setdefault(e, routed_get(e))
     rep["h_routed"] = check_hidden("e2e h_routed", out["h_routed"], ref["h_routed"], act,
                                    out["norm"],
-                                   lambda rj: (cfg.routed_fmt, getx(int(ref["idx"][rj])), rj[0]))
+                                   lambda rj: (cfg.routed_fmt, getx(int(ref["idx"][rj])), rj[0]),
+                                   cfg.act_quant)
     if cfg.shared_inter > 0:
         rep["h_shared"] = check_hidden("e2e h_shared", out["h_shared"], ref["h_shared"], act,
-                                       out["norm"], lambda r_: (cfg.shared_fmt, shared_h, r_[0]))
-    dh = np.abs(f64(out["h_routed"]) - f64(ref["h_routed"]))            # [R][K][I]
+                                       out["norm"], lambda r_: (cfg.shared_fmt, shared_h, r_[0]),
+                                       cfg.act_quant)
+
+    def down_input_dev(fmt, got_h, ref_h):
+        """|difference| of what the down projections see: the hidden rows, or with MXFP8
+        activations for an MXFP4 matrix their round trips (a one-step change of h can move a
+        quantisation step or a block scale)."""
+        a, b = f64(got_h), f64(ref_h)
+        if cfg.act_quant == "mxfp8" and fmt == "mxfp4":
+            sh = a.shape
+            a = np.stack([mx8_round_trip(v) for v in a.reshape(-1, sh[-1])]).reshape(sh)
+            b = np.stack([mx8_round_trip(v) for v in b.reshape(-1, sh[-1])]).reshape(sh)
+        return np.abs(a - b)
+
+    dh = down_input_dev(cfg.routed_fmt, out["h_routed"], ref["h_routed"])  # [R][K][I]
     w = np.abs(np.asarray(ref["weights"], np.float64))
     ext_routed = np.zeros((R, H))
     for e in np.unique(ref["idx"]):
@@ -520,7 +550,7 @@ def compare_end_to_end(cfg: synth.Config, out: Dict[str, np.ndarray], state_h, d
     d_routed = F32_TOL * np.maximum(np.abs(r64), rms) + ext_routed
     d_shared = 0.0
     if cfg.shared_inter > 0:
-        dhs = np.abs(f64(out["h_shared"]) - f64(ref["h_shared"]))        # [R][Is]
+        dhs = down_input_dev(cfg.shared_fmt, out["h_shared"], ref["h_shared"])  # [R][Is]
         ext_shared = np.zeros((R, H))
         if np.any(dhs):
             aw = np.abs(dequant(cfg.shared_fmt, shared_h["down"], shared_h.get("down_s")))

@@ -81,6 +81,7 @@ def test_invalid_shape_lists_every_reason():
     (dict(shared_inter=-32), "shared_inter=-32"),
     (dict(sinkhorn_iters=-1), "sinkhorn_iters=-1"),
     (dict(eps_norm=-1.0), "eps_hc / eps_norm"),
+    (dict(act_quant=7), "act_quant=7"),
 ])
 def test_each_shape_limit(kw, needle):
     with pytest.raises(B.MonoError) as e:
@@ -99,6 +100,20 @@ def test_on_chip_limits_are_unsupported_not_invalid():
                          None, P256)
     assert e.value.status == B.MONO_E_UNSUPPORTED
     assert "hidden-row buffer" in e.value.message
+
+
+def test_mxfp8_activations_need_mxfp4_routed_experts():
+    s = shape(rows=8, act_quant="mxfp8")
+    for call in (lambda L: B.mono_ffn_layer(s, L, None, P16, None, P16, None, P256),
+                 lambda L: B.mono_moe_experts(s, P16, P16, P16, L, P16, P16, P16, P256)):
+        with pytest.raises(B.MonoError) as e:
+            call(layer("q8_0", "mxfp4"))
+        assert e.value.status == B.MONO_E_UNSUPPORTED
+        assert "act_quant MONO_AQ_MXFP8 needs routed.fmt MONO_MXFP4" in e.value.message
+    # with MXFP4 routed experts the mode passes the checks (rows == 0: nothing is enqueued)
+    s0 = shape(rows=0, act_quant="mxfp8")
+    B.mono_ffn_layer(s0, layer("mxfp4", "bf16"), None, P16, None, P16, None, P256)
+    B.mono_moe_experts(s0, P16, P16, P16, layer("mxfp4", "mxfp4"), P16, P16, P16, P256)
 
 
 def test_rows_zero_is_ok_and_enqueues_nothing():

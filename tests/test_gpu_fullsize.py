@@ -8,7 +8,8 @@ Workloads: hidden 5120, 256 experts, top-8, inter 2048, shared inter 2048, rho 2
   * 8 rows, MXFP4 routed + bf16 shared experts, row 7 all zero, bias grouped by 32,
   * a chain of 8 bf16 layer halves at 1 row linked by the next-pre carry;
 and the draft routing shapes at the same widths: 128 experts with top-3 and 256 experts with
-top-6, each at 1 row (bf16 experts) and 6 rows (Q8_0 experts).
+top-6, each at 1 row (bf16 experts) and 6 rows (Q8_0 experts); and the 8-row MXFP4 workload with
+the activations of the MXFP4 experts quantised to MXFP8.
 """
 
 import numpy as np
@@ -27,7 +28,7 @@ def _host(cfg, layer):
     return synth.dense_host(cfg, layer), shared
 
 
-@pytest.mark.parametrize("ci", [2, 3, 4, *synth.DRAFT_CONFIGS])
+@pytest.mark.parametrize("ci", [2, 3, 4, *synth.DRAFT_CONFIGS, 10])
 def test_full_size_layer(ci):
     import torch
     import support
@@ -49,7 +50,7 @@ def test_full_size_layer(ci):
     e2e = support.compare_end_to_end(cfg, fused, synth.state_host(cfg, 5), d0,
                                      lambda e: synth.expert_host(cfg, 0, e), shared, d1["w_mix"])
     print(ci, "end-to-end", {k: v for k, v in e2e.items() if k != "ref"}, flush=True)
-    if ci == 4:
+    if ci in (4, 10):
         grp = int(np.argmax(d0["bias"][::32]))
         assert fused["idx"][7].tolist() == list(range(32 * grp, 32 * grp + cfg.top_k))
     del g

@@ -43,6 +43,18 @@ CASES = {
     "draft_e128_k3_r1": synth.CONFIGS[6].with_(hidden=512, inter=256, shared_inter=256),
     "draft_e128_k3_r6_q8": synth.CONFIGS[7].with_(hidden=512, inter=256, shared_inter=256),
     "e256_k6_r6_q8": synth.CONFIGS[9].with_(hidden=512, inter=256, shared_inter=256),
+    # MXFP8 activations for the MXFP4 experts: 8 rows with the zero row (bf16 shared), the
+    # one-row down flow (bf16 and MXFP4 shared), and MXFP4 or Q8_0 shared experts at 3 and 5 rows
+    "fp4_mx8_r8_zero_row": synth.CONFIGS[10].with_(hidden=512, n_experts=64, top_k=8, inter=256,
+                                                   shared_inter=256),
+    "fp4_mx8_r1": synth.CONFIGS[10].with_(rows=1, zero_rows=(), grouped_bias=False, **SMALL),
+    "fp4_mx8_r1_fp4_shared": synth.CONFIGS[10].with_(rows=1, zero_rows=(), grouped_bias=False,
+                                                     shared_fmt="mxfp4", **SMALL),
+    "fp4_mx8_r3_fp4_shared": synth.CONFIGS[10].with_(rows=3, zero_rows=(), grouped_bias=False,
+                                                     shared_fmt="mxfp4", **SMALL),
+    "fp4_mx8_r5_q8_shared": synth.CONFIGS[10].with_(rows=5, zero_rows=(), grouped_bias=False,
+                                                    shared_fmt="q8_0", hidden=576, n_experts=40,
+                                                    top_k=6, inter=96, shared_inter=160),
 }
 
 OUT_KEYS = ["mixes", "pre", "post", "comb", "x", "norm", "logits", "idx", "weights",
@@ -129,6 +141,29 @@ def test_fused_matches_free_running_oracle(name, runs):
         compared += "skipped" not in rep
         print(name, sample, {k: v for k, v in rep.items() if k != "ref"})
     assert compared >= 1, "both samples rest on near ties"
+
+
+@pytest.mark.parametrize("name", ["fp4_mx8_r8_zero_row", "fp4_mx8_r1_fp4_shared"])
+def test_mxfp8_mode_takes_effect(name, runs):
+    """The MXFP8 activations change the expert outputs by far more than the comparison
+    tolerance: the GPU's routed sum (and shared output, for an MXFP4 shared expert) sits within
+    tolerance of the oracle in the MXFP8 mode and far outside it from the unquantised oracle, both
+    fed the GPU's selection and hidden rows."""
+    import oracle
+    cfg, res = runs(name)
+    out = res[0][1]
+    st, d0, d1, shared = host_inputs(cfg, 0)
+    experts = {int(e): synth.expert_host(cfg, 0, int(e)) for e in np.unique(out["idx"])}
+    devs = {}
+    for aq in ("mxfp8", "none"):
+        s = oracle.shape_of(cfg.with_(act_quant=aq))
+        m = oracle.moe(s, None, out["idx"], out["weights"], cfg.routed_fmt, experts,
+                       cfg.shared_fmt, shared, out["h_routed"], out["h_shared"])
+        ref = m["routed"].astype(np.float64)
+        devs[aq] = np.max(np.abs(out["routed"] - ref) / np.maximum(np.abs(ref), 1e-2))
+    print(name, devs)
+    assert devs["mxfp8"] < 1e-4
+    assert devs["none"] > 30 * devs["mxfp8"] and devs["none"] > 1e-3
 
 
 def test_zero_row_follows_canonical_order(runs):
