@@ -498,7 +498,6 @@ struct Smem {
   float red[kWaves][kMaxRows];
   float rsum[kMaxRows];
   int sel_e[kMaxRows][kMaxTopK];
-  float sel_s[kMaxRows][kMaxTopK];
   float sel_w[kMaxRows][kMaxTopK];
   int U[kMaxUnion + 1];
   uint32_t umask[kMaxUnion + 1];
@@ -1369,10 +1368,13 @@ __device__ __forceinline__ bool gather_logits(const Params& p, const Smem& sm, i
  * hold it) and the owning lane pops its head. Returns false when the logits did not arrive. */
 template <int PER>
 __device__ __forceinline__ bool select_row(const Params& p, Smem& sm, int r, bool write_out,
-                                           bool check, uint32_t tag) {
+                                           bool check, uint32_t tag, int& e_lane, float& s_lane) {
   const int lane = threadIdx.x & 63, E = p.E, K = p.K;
   uint32_t kh[PER], kl[PER];
-  float sv[PER], zs[PER];
+  float sv[PER], zs[PER], bz[PER];
+  /* the lane's biases, read from LDS while the logits are still in flight */
+#pragma unroll
+  for (int c = 0; c < PER; ++c) bz[c] = lane + 64 * c < E ? sm.bias[lane + 64 * c] : 0.0f;
   const bool gathered = gather_logits<PER>(p, sm, r, check, tag, zs);
   if (lane == 0) __hip_atomic_store(&sm.lg_ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   if (!gathered) return false;
@@ -1387,7 +1389,7 @@ __device__ __forceinline__ bool select_row(const Params& p, Smem& sm, int r, boo
       const float z = zs[c];
       if (write_out) p.logits[(size_t)r * E + e] = z;
       const float sc = sqrtf(softplus_f32(z));
-      kh[c] = ord_f32(sc + sm.bias[e]);
+      kh[c] = ord_f32(sc + bz[c]);
       kl[c] = 0xFFFFFFFFu - (uint32_t)e;
       sv[c] = sc;
     }
@@ -1409,9 +1411,10 @@ __device__ __forceinline__ bool select_row(const Params& p, Smem& sm, int r, boo
     const bool win = kh[0] == mh && kl[0] == ml;
     const uint64_t who = __ballot(win);
     const float s_win = readlane(sv[0], (int)__builtin_ctzll(who));
-    if (lane == 0) {
-      sm.sel_e[r][j] = (int)(0xFFFFFFFFu - ml);
-      sm.sel_s[r][j] = s_win;
+    if (lane == 0) sm.sel_e[r][j] = (int)(0xFFFFFFFFu - ml);
+    if (lane == j) { /* pick j also stays in lane j */
+      e_lane = (int)(0xFFFFFFFFu - ml);
+      s_lane = s_win;
     }
     if (win) {
 #pragma unroll
@@ -1428,6 +1431,25 @@ __device__ __forceinline__ bool select_row(const Params& p, Smem& sm, int r, boo
   return true;
 }
 
+/* Routing weights of row r by the wave that selected it, pick j in lane j (e_lane, s_lane):
+ * sum = f32 sum of the picked scores in pick order, c = max(sum, 2^-14), w_j = (s_j / c) rho
+ * [ds4 router commit: sum, clamp, divide and scale as separate rounded ops]. */
+__device__ __forceinline__ void select_weights(const Params& p, Smem& sm, int r, int e_lane,
+                                               float s_lane, bool write_out) {
+  const int lane = threadIdx.x & 63, K = p.K;
+  float sum = 0.0f;
+  for (int j = 0; j < K; ++j) sum += readlane(s_lane, j);
+  const float c = fmaxf(sum, 6.103515625e-05f); /* 2^-14 */
+  if (lane < K) {
+    const float w = (s_lane / c) * p.rho;
+    sm.sel_w[r][lane] = w;
+    if (write_out) {
+      p.idx[r * K + lane] = e_lane;
+      p.weights[r * K + lane] = w;
+    }
+  }
+}
+
 /* Select, part 1: waves 0 .. min(R, 8) - 1 take rows r = wave, wave + 8, ... Needs sm.sel_ok
  * set to 1 beforehand (made visible by a __syncthreads); no workgroup barrier inside, so other
  * waves may do independent work meanwhile. */
@@ -1435,59 +1457,23 @@ __device__ __forceinline__ void select_rows(const Params& p, Smem& sm, bool writ
                                             uint32_t tag) {
   const int wave = threadIdx.x >> 6;
   for (int r = wave; r < p.R; r += kWaves) {
-    const bool ok = p.E <= 256 ? select_row<4>(p, sm, r, write_out, check, tag)
-                               : select_row<kMaxExperts / 64>(p, sm, r, write_out, check, tag);
+    int e_l;
+    float s_l;
+    const bool ok = p.E <= 256 ? select_row<4>(p, sm, r, write_out, check, tag, e_l, s_l)
+                               : select_row<kMaxExperts / 64>(p, sm, r, write_out, check, tag,
+                                                              e_l, s_l);
+    if (ok) select_weights(p, sm, r, e_l, s_l, write_out);
     if (!ok && (threadIdx.x & 63) == 0) sm.sel_ok = 0;
   }
 }
 
-/* Select, part 2 (after a __syncthreads that follows part 1): normalised, clamped and scaled
- * routing weights. Returns false (after reporting once) when some row's logits did not arrive
- * in time. */
-/* The weights of select_finish, without its barrier: threads 0 .. R - 1 (all in wave 0 when
- * R <= 64). Returns false (after reporting once) when some row's logits did not arrive. */
-__device__ __forceinline__ bool select_finish_nobar(const Params& p, Smem& sm, bool write_out) {
-  const int tid = threadIdx.x, K = p.K;
-  if (sm.sel_ok == 0) {
-    if (tid == 0) report_timeout(p, PH_ROUTER);
-    return false;
-  }
-  if (tid < p.R) {
-    const int r = tid;
-    float sum = 0.0f;
-    for (int j = 0; j < K; ++j) sum += sm.sel_s[r][j];
-    const float c = fmaxf(sum, 6.103515625e-05f); /* 2^-14 */
-    for (int j = 0; j < K; ++j) {
-      const float w = (sm.sel_s[r][j] / c) * p.rho;
-      sm.sel_w[r][j] = w;
-      if (write_out) {
-        p.idx[r * K + j] = sm.sel_e[r][j];
-        p.weights[r * K + j] = w;
-      }
-    }
-  }
-  return true;
-}
-
+/* Select, part 2 (after a __syncthreads that follows part 1; the weights are in sm.sel_w).
+ * Returns false (after reporting once) when some row's logits did not arrive in time. */
 __device__ __forceinline__ bool select_finish(const Params& p, Smem& sm, bool write_out) {
-  const int tid = threadIdx.x, K = p.K;
+  (void)write_out;
   if (sm.sel_ok == 0) {
-    if (tid == 0) report_timeout(p, PH_ROUTER);
+    if (threadIdx.x == 0) report_timeout(p, PH_ROUTER);
     return false;
-  }
-  if (tid < p.R) {
-    const int r = tid;
-    float sum = 0.0f;
-    for (int j = 0; j < K; ++j) sum += sm.sel_s[r][j];
-    const float c = fmaxf(sum, 6.103515625e-05f); /* 2^-14 */
-    for (int j = 0; j < K; ++j) {
-      const float w = (sm.sel_s[r][j] / c) * p.rho;
-      sm.sel_w[r][j] = w;
-      if (write_out) {
-        p.idx[r * K + j] = sm.sel_e[r][j];
-        p.weights[r * K + j] = w;
-      }
-    }
   }
   __syncthreads();
   return true;
@@ -1521,12 +1507,13 @@ __device__ __forceinline__ void load_selection(const Params& p, Smem& sm) {
  * is the shared expert (every row). Built by wave 0 alone from a bitmap of the selected
  * experts (LDS operations of one wave complete in order); every wave sees it after the
  * __syncthreads at the end. */
-__device__ __forceinline__ void plan_wave(const Params& p, Smem& sm) {
-  if (p.R == 1) {
-    /* one row: its k experts are distinct, so the plan is their ascending order; lane q < k
-     * ranks expert sel_e[0][q] among them (same result as the bitmap walk below) */
+/* One-row plan, by one wave: its k experts are distinct, so the plan is their ascending order;
+ * lane q < k holds pick q (expert e_lane) and ranks it among them (the same result as the
+ * bitmap walk of plan_wave). */
+__device__ __forceinline__ void plan_one_row(const Params& p, Smem& sm, int e_lane) {
+  {
     const int lane = threadIdx.x & 63, K = p.K;
-    const int e = lane < K ? sm.sel_e[0][lane] : 0x7FFFFFFF;
+    const int e = lane < K ? e_lane : 0x7FFFFFFF;
     int rank = 0;
     for (int t = 0; t < K; ++t) rank += __builtin_amdgcn_readlane(e, t) < e ? 1 : 0;
     for (int q = lane; q < (K + 1) * kMaxRows; q += 64) sm.uslot[q / kMaxRows][q % kMaxRows] = -1;
@@ -1541,6 +1528,21 @@ __device__ __forceinline__ void plan_wave(const Params& p, Smem& sm) {
       sm.uslot[K][0] = (int8_t)K;
       sm.nU = K;
     }
+  }
+}
+
+/* One-row finish of the select in the fused launch, by wave 0 with pick j in lane j
+ * (e_lane, s_lane): the weights, then the plan. */
+__device__ __forceinline__ void finish_one_row(const Params& p, Smem& sm, int e_lane,
+                                               float s_lane, bool write_out) {
+  select_weights(p, sm, 0, e_lane, s_lane, write_out);
+  plan_one_row(p, sm, e_lane);
+}
+
+__device__ __forceinline__ void plan_wave(const Params& p, Smem& sm) {
+  if (p.R == 1) {
+    const int lane = threadIdx.x & 63;
+    plan_one_row(p, sm, lane < p.K ? sm.sel_e[0][lane] : 0);
     return;
   }
   {
@@ -3415,16 +3417,18 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
     /* one row: wave 0 selects while the other waves take the shared expert's rows, which they
      * start once wave 0 has gathered the logits: their loads would otherwise queue ahead of its
      * polls (bounded wait; wave 0 sets the flag whether or not the logits arrived) */
-    select_rows(p, sm, blockIdx.x == 0, true, tag);
     if (threadIdx.x < 64) {
-      /* wave 0 finishes the select and builds the plan without waiting for the other waves'
-       * shared rows, then publishes it through sm.plan_ready (1 ready, 2 the logits did not
-       * arrive). The fences order the lanes' LDS accesses: lane 0 wrote the selection. */
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-      const bool ok = select_finish_nobar(p, sm, blockIdx.x == 0);
+      /* wave 0 selects, finishes the select and builds the plan with pick j held in lane j,
+       * without waiting for the other waves' shared rows, then publishes the plan through
+       * sm.plan_ready (1 ready, 2 the logits did not arrive) */
+      int e_l = 0;
+      float s_l = 0.0f;
+      const bool ok =
+          p.E <= 256 ? select_row<4>(p, sm, 0, blockIdx.x == 0, true, tag, e_l, s_l)
+                     : select_row<kMaxExperts / 64>(p, sm, 0, blockIdx.x == 0, true, tag, e_l, s_l);
+      if (!ok && threadIdx.x == 0) report_timeout(p, PH_ROUTER);
       stamp(p, tr, 7);
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-      if (ok) plan_wave(p, sm);
+      if (ok) finish_one_row(p, sm, e_l, s_l, blockIdx.x == 0);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       if (threadIdx.x == 0)
         __hip_atomic_store(&sm.plan_ready, ok ? 1 : 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
