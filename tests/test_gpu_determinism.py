@@ -14,6 +14,9 @@ CASES = {
                                       shared_inter=512),
     "q8_r2": synth.CONFIGS[3].with_(rows=2, hidden=1024, n_experts=64, top_k=8, inter=512,
                                     shared_inter=512),
+    "fp4_mx8_r3": synth.CONFIGS[10].with_(rows=3, zero_rows=(), grouped_bias=False,
+                                          shared_fmt="mxfp4", hidden=1024, n_experts=64,
+                                          top_k=8, inter=512, shared_inter=512),
 }
 
 

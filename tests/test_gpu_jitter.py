@@ -21,6 +21,14 @@ CASES = {
                                              inter=96, shared_inter=160),
     "full_bf16_r1": synth.CONFIGS[2],
     "full_q8_r6": synth.CONFIGS[3],
+    # MXFP8 activations: the in-place round trips of the staged hidden rows (by the staging
+    # wave between workgroup fences in the one-row flow, by the workgroup behind barriers at
+    # several rows) and of the norm rows
+    "fp4_mx8_r1_fp4_shared": synth.CONFIGS[10].with_(rows=1, zero_rows=(), grouped_bias=False,
+                                                     shared_fmt="mxfp4", **SMALL),
+    "fp4_mx8_r8_zero_row": synth.CONFIGS[10].with_(hidden=512, n_experts=64, top_k=8, inter=256,
+                                                   shared_inter=256),
+    "full_fp4_mx8_r8": synth.CONFIGS[10],
 }
 KEYS = ["mixes", "pre", "post", "comb", "x", "norm", "logits", "idx", "weights", "h_routed",
         "h_shared", "shared", "routed", "block", "new_state", "carry"]
