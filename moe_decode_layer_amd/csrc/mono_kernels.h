@@ -3132,6 +3132,48 @@ __device__ __forceinline__ bool reduce_carry(const Params& p, Smem& sm, int q, b
  * slice before every workgroup has read the whole input (mix partials and collapse): each
  * workgroup publishes the launch tag in pre_done[wg] after its collapse, and the expand waits
  * (bounded) until all of them carry it. Whole workgroup; returns false on expiry. */
+/* Every carry output by the last workgroup of the per-stage expand to arrive (all partials are
+ * complete): wave w takes outputs q = w, w + 8, ..., with reduce_carry's arithmetic (lane L adds
+ * workgroups L, L + 64, ... in turn, then the wave sum), so the per-stage and fused launches
+ * give the same bits; the outputs proceed side by side instead of one workgroup reduction
+ * (two barriers and a round of loads) after another. */
+__device__ __forceinline__ void reduce_carry_waves(const Params& p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, G = gridDim.x;
+  const int NQ = p.R * kNCarry;
+  constexpr int QB = 4, KW = (kMaxGrid + 63) / 64; /* outputs per round, loads per output */
+  const __amdgpu_buffer_rsrc_t cp = coh_region(p.carry_part, (size_t)NQ * G * 8);
+  for (int q0 = wave; q0 < NQ; q0 += kWaves * QB) {
+    /* all loads of the round first (past the end: a repeated valid address, unused) */
+    uint32_t v[QB][KW];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int q = q0 + b * kWaves < NQ ? q0 + b * kWaves : q0;
+#pragma unroll
+      for (int k = 0; k < KW; ++k) {
+        if (64 * k >= G) break; /* uniform */
+        const int w = lane + 64 * k < G ? lane + 64 * k : lane;
+        v[b][k] = coh_b64(cp, (uint32_t)(((size_t)q * G + w) * 8)).x;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int q = q0 + b * kWaves;
+      if (q >= NQ) break;
+      float t = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KW; ++k) {
+        if (64 * k >= G) break; /* uniform */
+        if (lane + 64 * k < G) t += __uint_as_float(v[b][k]);
+      }
+      t = wave_sum(t);
+      if (lane == 0) {
+        p.carry_out[q] = t;
+        if (p.carry_ws) p.carry_ws[q] = t;
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ bool wait_pre_done(const Params& p, Smem& sm, uint32_t tag) {
   const int G = gridDim.x;
   const __amdgpu_buffer_rsrc_t rs = coh_region(p.pre_done, (size_t)G * 8);
@@ -3241,7 +3283,7 @@ __device__ __forceinline__ void ph_expand(const Params& p, Smem& sm, const float
     for (int q = blockIdx.x; q < R * kNCarry; q += gridDim.x)
       if (!reduce_carry(p, sm, q, true, tag)) return;
   } else if (arrive_last_single(p, sm)) {
-    for (int q = 0; q < R * kNCarry; ++q) reduce_carry(p, sm, q, false, 0u);
+    reduce_carry_waves(p);
   }
 }
 
