@@ -55,6 +55,14 @@ CASES = {
     "fp4_mx8_r5_q8_shared": synth.CONFIGS[10].with_(rows=5, zero_rows=(), grouped_bias=False,
                                                     shared_fmt="q8_0", hidden=576, n_experts=40,
                                                     top_k=6, inter=96, shared_inter=160),
+    # no shared expert, and one row whose 17 hidden rows exceed the one-row flow's LDS room (the
+    # grouped per-slice down phase stages and round-trips them)
+    "fp4_mx8_r4_no_shared": synth.CONFIGS[10].with_(rows=4, zero_rows=(), grouped_bias=False,
+                                                    hidden=512, n_experts=32, top_k=4, inter=256,
+                                                    shared_inter=0),
+    "fp4_mx8_r1_k16_wide": synth.CONFIGS[10].with_(rows=1, zero_rows=(), grouped_bias=False,
+                                                   hidden=512, n_experts=64, top_k=16, inter=2560,
+                                                   shared_inter=2560),
 }
 
 OUT_KEYS = ["mixes", "pre", "post", "comb", "x", "norm", "logits", "idx", "weights",
