@@ -635,46 +635,64 @@ __device__ __forceinline__ int wave_major_id() {
  * part[t][r][24] = sum s^2 over the chunk. */
 template <int ACT, int RMAX>
 __device__ __forceinline__ void ph_mix_partials(const Params& p, uint32_t tag, bool skip) {
-  const int n = 4 * p.H, nch = n / kMixChunk;
+  const int n = 4 * p.H, nch = (n + kMixChunk - 1) / kMixChunk;
   const int lane = threadIdx.x & 63;
   const int nwt = gridDim.x * kWaves;
   /* task = (chunk, row, group of kMixGroup outputs; the last group also takes the sum of
-   * squares), so a wave loads kMixGroup weight rows and reduces at most kMixGroup + 1 sums */
-  constexpr int NG = kNMix / kMixGroup;
+   * squares), so a wave loads kMixGroup weight rows and reduces at most kMixGroup + 1 sums.
+   * A lane takes positions base + 256 h + 0..3 for the halves h of the chunk that exist (n is a
+   * multiple of 256, so the last chunk may have one half only) */
+  constexpr int NG = kNMix / kMixGroup, NH = kMixChunk / 256;
   for (int t = wave_major_id(); t < nch * p.R * NG; t += nwt) {
     const int g = t % NG, ch = t / NG / p.R, r = t / NG % p.R;
     const int base = ch * kMixChunk + lane * 4;
-    float4 w[kMixGroup];
+    float4 w[NH][kMixGroup];
+    float s[NH][4];
 #pragma unroll
-    for (int j = 0; j < kMixGroup; ++j)
-      w[j] = *reinterpret_cast<const float4*>(p.w_mix + (size_t)(g * kMixGroup + j) * n + base);
-    float s[4];
-    if (ACT == F32) {
-      const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(p.state) +
-                                                        (size_t)r * n + base);
-      s[0] = v.x; s[1] = v.y; s[2] = v.z; s[3] = v.w;
-    } else {
-      const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.state) +
-                                                      (size_t)r * n + base);
-      s[0] = bf2f(v.x & 0xFFFFu); s[1] = bf2f(v.x >> 16);
-      s[2] = bf2f(v.y & 0xFFFFu); s[3] = bf2f(v.y >> 16);
+    for (int h = 0; h < NH; ++h) {
+      const int b = base + 256 * h;
+      const bool in = ch * kMixChunk + 256 * h < n; /* uniform */
+#pragma unroll
+      for (int j = 0; j < kMixGroup; ++j)
+        w[h][j] = in ? *reinterpret_cast<const float4*>(p.w_mix + (size_t)(g * kMixGroup + j) * n + b)
+                     : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (!in) {
+        s[h][0] = s[h][1] = s[h][2] = s[h][3] = 0.0f;
+      } else if (ACT == F32) {
+        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(p.state) +
+                                                          (size_t)r * n + b);
+        s[h][0] = v.x; s[h][1] = v.y; s[h][2] = v.z; s[h][3] = v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.state) +
+                                                        (size_t)r * n + b);
+        s[h][0] = bf2f(v.x & 0xFFFFu); s[h][1] = bf2f(v.x >> 16);
+        s[h][2] = bf2f(v.y & 0xFFFFu); s[h][3] = bf2f(v.y >> 16);
+      }
     }
     uint64_t* out = p.mix_part + ((size_t)ch * p.R + r) * kNCarry;
 #pragma unroll
     for (int j = 0; j < kMixGroup; ++j) {
-      float a = w[j].x * s[0];
-      a = fmaf(w[j].y, s[1], a);
-      a = fmaf(w[j].z, s[2], a);
-      a = fmaf(w[j].w, s[3], a);
+      float a = 0.0f;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        a = fmaf(w[h][j].x, s[h][0], a);
+        a = fmaf(w[h][j].y, s[h][1], a);
+        a = fmaf(w[h][j].z, s[h][2], a);
+        a = fmaf(w[h][j].w, s[h][3], a);
+      }
       const float tot = wave_sum(a);
       if (lane == 0 && !skip)
         st_coh(out + g * kMixGroup + j, ((uint64_t)tag << 32) | __float_as_uint(tot));
     }
     if (g != NG - 1) continue;
-    float ss = s[0] * s[0];
-    ss = fmaf(s[1], s[1], ss);
-    ss = fmaf(s[2], s[2], ss);
-    ss = fmaf(s[3], s[3], ss);
+    float ss = 0.0f;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      ss = fmaf(s[h][0], s[h][0], ss);
+      ss = fmaf(s[h][1], s[h][1], ss);
+      ss = fmaf(s[h][2], s[h][2], ss);
+      ss = fmaf(s[h][3], s[h][3], ss);
+    }
     const float tot = wave_sum(ss);
     if (lane == 0 && !skip) st_coh(out + kNMix, ((uint64_t)tag << 32) | __float_as_uint(tot));
   }
@@ -744,7 +762,7 @@ template <int ACT, int RMAX>
 __device__ __forceinline__ bool ph_hc_pre(const Params& p, Smem& sm, bool write_out, bool check,
                                           uint32_t tag) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int R = p.R, H = p.H, n = 4 * H, nch = n / kMixChunk;
+  const int R = p.R, H = p.H, n = 4 * H, nch = (n + kMixChunk - 1) / kMixChunk;
   constexpr int VE = ACT == F32 ? 4 : 8; /* elements per 16-byte state load */
   const size_t ab = ACT == F32 ? 4 : 2;
   /* raw mix sums: the tagged partials [chunk][row][25] are copied into LDS with contiguous
@@ -3409,7 +3427,7 @@ __global__ void __launch_bounds__(kBlock, 1) k_ffn_layer(Params p) {
   RouterRegs rpre;
   int t0 = 0; /* waves below t0 / 64 have a mix-partial task; the others copy the pre inputs */
   if (!p.carry_in) {
-    const int ntask = (4 * p.H / kMixChunk) * p.R * (kNMix / kMixGroup);
+    const int ntask = ((4 * p.H + kMixChunk - 1) / kMixChunk) * p.R * (kNMix / kMixGroup);
     const int busy = ntask > (int)blockIdx.x ? (ntask - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
     t0 = busy < kWaves ? busy * 64 : 0;
     ph_mix_partials<ACT, RMAX>(p, tag, sm.skip_phase == PH_MIX);
