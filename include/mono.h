@@ -65,15 +65,6 @@ typedef enum {
   MONO_E_TIMEOUT = -4      /* a device-side bounded wait expired (mono_workspace_poll) */
 } mono_status;
 
-/* Shape of one layer-half step. Limits (checked on the host, every failure listed):
- *   0 <= rows <= 8; n_streams == 4; hidden a positive multiple of 64; inter a positive multiple
- *   of 32 and shared_inter a non-negative multiple of 32; 1 <= top_k <= 16 and
- *   top_k <= n_experts <= 512; act MONO_F32 or MONO_BF16; 0 <= sinkhorn_iters <= 1000;
- *   routed_scale finite; eps_hc, eps_norm >= 0.
- *   On-chip buffers (ab = 4 for f32, 2 for bf16 activations): (rows + 1) * hidden * ab <=
- *   114688 bytes, rows * max(inter, shared_inter) * ab <= 81920 bytes and
- *   max(inter, shared_inter) * ab <= 16384 bytes, and the slice of hidden positions one
- *   workgroup expands must fit its LDS on the current device (MONO_E_UNSUPPORTED otherwise). */
 /* Activation quantisation of the expert matrix-vector products [vLLM "[ROCm][Perf][GLM-5] Fused
  * sparse-layer decode via AITER MonoKernel", Details, Numerics: the activations entering the
  * MXFP4 experts are quantised to MXFP8]. With MONO_AQ_MXFP8 the input of every matrix stored in
@@ -85,6 +76,16 @@ typedef enum {
  * Used by mono_moe_experts, mono_ffn_layer and mono_ffn_layer_static; the other calls ignore it. */
 typedef enum { MONO_AQ_NONE = 0, MONO_AQ_MXFP8 = 1 } mono_act_quant;
 
+/* Shape of one layer-half step. Limits (checked on the host, every failure listed):
+ *   0 <= rows <= 8; n_streams == 4; hidden a positive multiple of 64; inter a positive multiple
+ *   of 32 and shared_inter a non-negative multiple of 32; 1 <= top_k <= 16 and
+ *   top_k <= n_experts <= 512; act MONO_F32 or MONO_BF16; 0 <= sinkhorn_iters <= 1000;
+ *   routed_scale finite; eps_hc, eps_norm >= 0; act_quant MONO_AQ_NONE or MONO_AQ_MXFP8, the
+ *   latter with routed.fmt MONO_MXFP4 (checked by the calls that take the layer).
+ *   On-chip buffers (ab = 4 for f32, 2 for bf16 activations): (rows + 1) * hidden * ab <=
+ *   114688 bytes, rows * max(inter, shared_inter) * ab <= 81920 bytes and
+ *   max(inter, shared_inter) * ab <= 16384 bytes, and the slice of hidden positions one
+ *   workgroup expands must fit its LDS on the current device (MONO_E_UNSUPPORTED otherwise). */
 typedef struct {
   int rows;         /* R: decode rows (tokens) in the step */
   int hidden;       /* H */
